@@ -1,0 +1,63 @@
+"""Sensitivity of the pins: plant one plausible mistake at a time in a copy of
+oracle.c (CPU only, in a temporary directory), rebuild it, and require that
+at least one pin fails.  Every mutation keeps all memory accesses in bounds."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("conv_taps_reversed", "(double)w[d * K + k] * (double)x[(b * L + t - k) * D + d]",
+     "(double)w[d * K + (K - 1 - k)] * (double)x[(b * L + t - k) * D + d]"),
+    ("conv_bias_dropped", "double acc = bias ? (double)bias[d] : 0.0;", "double acc = 0.0;"),
+    ("conv_not_causal_at_k", "if (t >= k) acc +=", "if (t > k) acc +="),
+    ("silu_sign", "return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    ("softplus_no_abs", "log1p(exp(-fabs(v)))", "log1p(exp(-v))"),
+    ("clamp_lo_moved", "A_LOG_LO = -10.0;", "A_LOG_LO = -9.0;"),
+    ("clamp_hi_moved", "A_LOG_HI = 5.0;", "A_LOG_HI = 6.0;"),
+    ("a_sign", "    return -exp(c);", "    return exp(-c);"),
+    ("zoh_missing_div_a", "return expm1(dv * A) / A * Bv;", "return expm1(dv * A) * Bv;"),
+    ("zoh_wrong_sign", "return expm1(dv * A) / A * Bv;", "return expm1(-dv * A) / A * Bv;"),
+    ("euler_missing_dv", "    return dv * Bv;", "    return Bv;"),
+    ("no_decay", "h[n] = ab * h[n] + bb * uv;", "h[n] = h[n] + bb * uv;"),
+    ("output_uses_B", "acc += (double)a->Cm[r * N + n] * h[n];",
+     "acc += (double)a->Bm[r * N + n] * h[n];"),
+    ("skip_dropped", "double acc = Dd * uv;", "double acc = 0.0;"),
+    ("gate_dropped", "y[t * y_stride] = a->z ? acc * silu((double)a->z[r * D + d]) : acc;",
+     "y[t * y_stride] = acc;"),
+    ("hcache_before_update",
+     "h[n] = ab * h[n] + bb * uv;\n            if (hc) hc[t * hc_stride + n] = h[n];",
+     "if (hc) hc[t * hc_stride + n] = h[n];\n            h[n] = ab * h[n] + bb * uv;"),
+    ("row_ignores_batch", "const int64_t r = b * L + t;", "const int64_t r = t;"),
+    ("h0_transposed", "a->h0[(b * D + d) * N + n]", "a->h0[(d * a->B + b) * N + n]"),
+    ("step_window_reversed", "acc += (double)w_conv[d * K + k] * win[S - k];",
+     "acc += (double)w_conv[d * K + k] * win[k - 1];"),
+    ("step_state_not_shifted", "(j + 1 < S) ? win[j + 1] : xv", "(j + 1 < S) ? win[j] : xv"),
+    ("step_dt_ignored_in_input", "const double bb = b_bar(disc, dv, A, (double)Bm[b * N + n]);",
+     "const double bb = b_bar(disc, 1.0, A, (double)Bm[b * N + n]);"),
+]
+
+
+@pytest.fixture(scope="module")
+def src():
+    with open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, src, name, old, new):
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(path), str(tmp_path / "liboracle_mut.so")))
+    orc = oracle.Bound(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError) as e:  # noqa: PERF203
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
