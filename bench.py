@@ -1,0 +1,162 @@
+"""Throughput of the Mamba-1 block core on one MI355X.
+
+One step = one pass of the whole hot path over one batch: causal depthwise
+conv1d + SiLU, softplus(delta), clamped A, discretisation, selective scan,
+y = sum_n C h + D u, SiLU(z) gate -- the fused mss_mamba1_core kernel -- on the
+4 x 8192 x 5120 (d_state 16, d_conv 4) workload of a 2.8B-class Mamba-1
+block, inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--disc zoh|euler] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, AMD published
+METRIC = "selective-scan M·D elements/s and achieved HBM GB/s (% of peak), 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mamba1_core_b4_l8192_d5120.json")
+KERNEL_SOURCES = ("scan_kernel.hip", "device_math.h", "launch.h")
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mamba_selective_scan_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the fused kernel must move: x, delta, z in and y out per (m, d);
+    B and C per (m, n); the per-channel parameters once."""
+    M, D, N, K = w.M, w.d_inner, w.d_state, w.d_conv
+    return 4 * (4 * M * D + 2 * M * N + D * N + D * (K + 2))
+
+
+def measured_traffic(digest: str):
+    """HBM bytes per launch from rocprofv3 counters, if they were taken on this
+    exact kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, disc, target_s=15.0):
+    """The oracle as it stands, on a bounded sample of whole (b, d) columns of
+    the same workload, on all host cores it may use."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    allcols = w.batch * w.d_inner
+
+    def run(ncols):
+        cols = np.sort(rng.choice(allcols, size=ncols, replace=False))
+        t0 = time.perf_counter()
+        oracle.mamba1_core(inp["x"], inp["w_conv"], inp["b_conv"], inp["delta"], inp["A_log"],
+                           inp["B"], inp["C"], inp["D_vec"], inp["z"], None, batch=w.batch,
+                           seq_len=w.seq_len, disc=disc, cols=cols, nthreads=cores)
+        return time.perf_counter() - t0
+
+    n0 = 4 * cores
+    t = run(n0)
+    ncols = int(min(allcols, max(n0, n0 * target_s / max(t, 1e-3))))
+    ncols = max(cores, ncols // cores * cores)
+    t = run(ncols)
+    el = ncols * w.seq_len
+    return {"value": el / t, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"{ncols} whole (b,d) columns x {w.seq_len} steps of the same workload "
+                      f"({el} of {w.M * w.d_inner} M*D elements), fp64 C, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--disc", default="zoh", choices=("zoh", "euler"))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+
+    w = gen.MAMBA_2P8B
+    inp = gen.generate(w)
+    d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    y = torch.empty((w.M, w.d_inner), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                        d["D_vec"], d["z"], None, batch=w.batch, seq_len=w.seq_len,
+                        disc=args.disc, out=y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    elems = w.M * w.d_inner
+    value = elems / (ms_per_step / 1e3)
+
+    abytes = algorithmic_bytes(w)
+    achieved = abytes / (kern_ms / 1e3) / 1e9
+    digest = kernel_digest()
+    traffic = measured_traffic(digest)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+                   "d_inner": w.d_inner, "d_state": w.d_state, "d_conv": w.d_conv,
+                   "disc": args.disc, "h_cache": False, "kernel": "mss_mamba1_core (fused)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel_ms": kern_ms, "algorithmic_bytes": abytes,
+                     "kernel_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.disc)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

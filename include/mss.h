@@ -1,0 +1,141 @@
+/*
+ * mss.h -- C ABI of libmss: the data-parallel core of a Mamba-1 (S6) block on
+ * AMD Instinct MI355X (gfx950), hand-written HIP.
+ *
+ * The operation is the one the pages of the npm package
+ * "@seanhogg/builderforce-memory-engine" define in the diff
+ * 2026.7.12 -> 2026.9.27, file src/training/mamba1_cpu.ts, function
+ * mamba1CpuForward, steps 4 (causal depthwise conv1d), 5 (SiLU), 8 (selective
+ * scan with softplus(delta), A = -exp(clamp(A_log, -10, 5)), exponential
+ * discretisation, recurrence, y = sum_n C h + D u) and 9 (gate by SiLU(z)),
+ * with the layouts listed in that file's header comment.  The GPU dispatch
+ * of the same computation (conv1d_forward, forward_scan, forward_reduce and
+ * the h_cache binding) is in the diff 2026.7.14 -> 2026.9.28, file
+ * src/model/mamba1_block.ts, Mamba1Block.forward.
+ *
+ * Symbols: B = batch, L = seq_len, M = B * L, D = d_inner, N = d_state,
+ * K = d_conv.  Row r = b * L + t.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to dense, row-major fp32 arrays
+ *     on the current HIP device, allocated and owned by the caller.  The
+ *     library allocates nothing, keeps no device state and never frees a
+ *     caller buffer.
+ *   - Every pointer must be 16-byte aligned (MSS_EALIGN otherwise).
+ *   - Outputs may not overlap any input (MSS_EALIAS), except the state
+ *     buffers of mss_selective_step, which are updated in place by design.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *     returns without synchronising.  Arguments are validated before any
+ *     launch; a call that returns an error has written nothing.
+ *   - A zero size (B, L or D = 0) is valid and launches nothing, except that
+ *     a sequence of length 0 still defines h_last (= h0, or zeros).
+ *   - Limits: 1 <= N <= 16; 1 <= K <= 8.  Dimensions are int64; element
+ *     offsets are computed in 64 bits.
+ *   - NaN or Inf inputs are outside the contract: the kernels terminate and
+ *     write every output, but the values are unspecified.
+ *   - Calls on different streams may run concurrently; they share nothing.
+ */
+#ifndef MSS_H
+#define MSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSS_VERSION 1
+
+/* Status codes. */
+#define MSS_OK 0
+#define MSS_EINVAL (-1)     /* null required pointer, bad size or limit, bad struct_size, bad disc */
+#define MSS_EALIGN (-2)     /* a pointer is not 16-byte aligned */
+#define MSS_EALIAS (-3)     /* an output overlaps an input */
+#define MSS_EHIP (-5)       /* a HIP runtime call or kernel launch failed; see mss_last_hip_error */
+
+/* Problem sizes.  `struct_size` must be sizeof(mss_dims): it guards against a
+ * caller built against a different layout of this struct. */
+typedef struct mss_dims {
+    int32_t struct_size;
+    int32_t reserved;       /* must be 0 */
+    int64_t batch;          /* B */
+    int64_t seq_len;        /* L (ignored by mss_selective_step) */
+    int64_t d_inner;        /* D */
+    int64_t d_state;        /* N, 1..16 */
+    int64_t d_conv;         /* K, 1..8 (ignored by mss_selective_scan) */
+} mss_dims;
+
+/* Discretisation of the input term (the caller must choose; no default).
+ *   MSS_DISC_ZOH:   bBar = ((exp(dv*A) - 1) / A) * B, as the pages' scan
+ *                   computes it (mamba1CpuForward step 8; its backward pass
+ *                   differentiates the same form).
+ *   MSS_DISC_EULER: bBar = dv * B (the simplified form). */
+#define MSS_DISC_ZOH 0
+#define MSS_DISC_EULER 1
+
+/* Steps 4 + 5: u = SiLU(b_conv[d] + sum_{k<K, k<=t} w_conv[d*K + k] * x[b, t-k, d]).
+ * Tap k = 0 multiplies the current step; there is no contribution from
+ * before t = 0 of each batch row, and none across batch rows.
+ *   x      (M, D)  in
+ *   w_conv (D, K)  in
+ *   b_conv (D)     in, may be NULL (= 0)
+ *   u      (M, D)  out                                                      */
+int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv,
+                    const float* b_conv, float* u, hipStream_t stream);
+
+/* Steps 8 + 9 on a given u:
+ *   dv = softplus(delta) = max(delta, 0) + log1p(exp(-|delta|))
+ *   A[d,n] = -exp(clamp(A_log[d,n], -10, 5)),  aBar = exp(dv * A)
+ *   h_t = aBar * h_{t-1} + bBar(disc) * u_t      (h_{-1} = h0, or 0)
+ *   y_t = (D_vec[d] * u_t + sum_n C[r,n] * h_t[n]) * SiLU(z_t)
+ *   u, delta, z, y (M, D);  A_log (D, N);  B, C (M, N);  D_vec (D);
+ *   h0, h_last (B, D, N);  h_cache (B, L, D, N) = h_t after the update of step t.
+ *   Optional (NULL allowed): D_vec (= 0), z (ungated output), h0 (= 0),
+ *   h_cache, h_last.  Required: u, delta, A_log, B, C, y.
+ *   The carried state between time segments processed in parallel drops
+ *   contributions that have decayed by more than 2^-30 (see the design
+ *   notes); the result is otherwise the plain recurrence in fp32.          */
+int mss_selective_scan(const mss_dims* dims, int disc, const float* u, const float* delta,
+                       const float* A_log, const float* B, const float* C, const float* D_vec,
+                       const float* z, const float* h0, float* y, float* h_cache,
+                       float* h_last, hipStream_t stream);
+
+/* Steps 4, 5, 8 and 9 fused into one kernel: mss_conv1d_silu followed by
+ * mss_selective_scan, without materialising u.  Same arguments and layouts;
+ * x (M, D), w_conv (D, K), b_conv (D, may be NULL) replace u.             */
+int mss_mamba1_core(const mss_dims* dims, int disc, const float* x, const float* w_conv,
+                    const float* b_conv, const float* delta, const float* A_log,
+                    const float* B, const float* C, const float* D_vec, const float* z,
+                    const float* h0, float* y, float* h_cache, float* h_last,
+                    hipStream_t stream);
+
+/* One single-token recurrent step (decode) with carried state; the plainest
+ * reading of steps 4-9 for L = 1 with the conv window and h carried over.
+ *   x, z, delta, y (B, D);  B, C (B, N);  A_log (D, N);  D_vec (D);
+ *   w_conv (D, K);  b_conv (D);
+ *   conv_state (B, K-1, D) in/out: the K-1 previous inputs, oldest first;
+ *     tap k >= 1 multiplies conv_state[K-1-k]; afterwards the window is
+ *     shifted by one and x appended.  May be NULL only when K == 1.
+ *   h (B, D, N) in/out: the scan state, updated in place.
+ *   Optional: D_vec, z, b_conv (NULL = 0 / ungated / 0).              */
+int mss_selective_step(const mss_dims* dims, int disc, const float* x, const float* z,
+                       const float* delta, const float* A_log, const float* B, const float* C,
+                       const float* D_vec, const float* w_conv, const float* b_conv,
+                       float* conv_state, float* h, float* y, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* mss_strerror(int status);
+
+/* MSS_VERSION of the library that was loaded. */
+int mss_version(void);
+
+/* The hipError_t of the last MSS_EHIP returned on the calling thread. */
+int mss_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSS_H */

@@ -1,0 +1,203 @@
+"""MI355X-native Mamba-1 (S6) block core: Python binding of libmss.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmss.so`` (built in-tree by ``build.py``); PyTorch supplies
+device memory and the current stream.  There is no fallback: if the library
+is missing or a call fails, an exception is raised.
+
+Layouts (fp32, contiguous, on the current CUDA/HIP device):
+  x, z, delta, u, y : (batch*seq_len, D)     B, C : (batch*seq_len, N)
+  A_log : (D, N)   D_vec, b_conv : (D,)   w_conv : (D, K)
+  h0, h_last : (batch, D, N)   h_cache : (batch, seq_len, D, N)
+Single-token step: x, z, delta, y : (batch, D); B, C : (batch, N);
+  conv_state : (batch, K-1, D) oldest first; h : (batch, D, N).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import inputs  # noqa: F401  (seeded synthetic inputs; no method arithmetic)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmss.so")
+
+ZOH = 0
+EULER = 1
+_DISC = {"zoh": ZOH, "euler": EULER, ZOH: ZOH, EULER: EULER}
+
+MSS_OK = 0
+
+
+class MssError(RuntimeError):
+    def __init__(self, fn, status, msg, hip_error=0):
+        super().__init__(f"{fn} failed: status {status} ({msg})"
+                         + (f", hipError {hip_error}" if hip_error else ""))
+        self.status = status
+        self.hip_error = hip_error
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("d_conv", ctypes.c_int64)]
+
+
+def make_dims(batch, seq_len, d_inner, d_state, d_conv=1) -> Dims:
+    return Dims(ctypes.sizeof(Dims), 0, batch, seq_len, d_inner, d_state, d_conv)
+
+
+EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_selective_step",
+           "mss_strerror", "mss_version", "mss_last_hip_error")
+
+_lib = None
+
+
+def lib():
+    """The loaded libmss (ctypes).  Raises if the HIP library is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mamba_selective_scan_causal_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        dp = ctypes.POINTER(Dims)
+        L.mss_conv1d_silu.argtypes = [dp, p, p, p, p, p]
+        L.mss_selective_scan.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p]
+        L.mss_mamba1_core.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p, p, p]
+        L.mss_selective_step.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p, p]
+        for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
+                  "mss_selective_step", "mss_version", "mss_last_hip_error"):
+            getattr(L, f).restype = ctypes.c_int
+        L.mss_strerror.argtypes = [ctypes.c_int]
+        L.mss_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != MSS_OK:
+        L = lib()
+        raise MssError(fn, status, L.mss_strerror(status).decode(), L.mss_last_hip_error())
+
+
+def _disc(disc) -> int:
+    key = disc.lower() if isinstance(disc, str) else disc
+    if key not in _DISC:
+        raise ValueError("disc must be 'zoh' or 'euler'")
+    return _DISC[key]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, name, shape, required=True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _empty(shape, like):
+    return _torch().empty(shape, dtype=like.dtype, device=like.device)
+
+
+def conv1d_silu(x, w_conv, b_conv=None, *, batch, seq_len, out=None, stream=None):
+    """u = SiLU(causal depthwise conv1d(x) + b_conv), (batch*seq_len, D)."""
+    D, K = w_conv.shape
+    M = batch * seq_len
+    u = out if out is not None else _empty((M, D), x)
+    dims = make_dims(batch, seq_len, D, 1, K)
+    _check("mss_conv1d_silu", lib().mss_conv1d_silu(
+        ctypes.byref(dims), _ptr(x, "x", (M, D)), _ptr(w_conv, "w_conv", (D, K)),
+        _ptr(b_conv, "b_conv", (D,), False), _ptr(u, "u", (M, D)), _stream(stream)))
+    return u
+
+
+def _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last):
+    M = batch * seq_len
+    y = out if out is not None else _empty((M, D), x)
+    hc = (h_cache if not isinstance(h_cache, bool) else
+          (_empty((batch, seq_len, D, N), x) if h_cache else None))
+    hl = (h_last if not isinstance(h_last, bool) else
+          (_empty((batch, D, N), x) if h_last else None))
+    return y, hc, hl
+
+
+def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch, seq_len, disc,
+                   h_cache=False, h_last=False, out=None, stream=None):
+    """Selective scan + gate on a given u.  Returns (y, h_cache, h_last).
+
+    ``h_cache`` / ``h_last``: False (skip), True (allocate) or an output tensor."""
+    D, N = A_log.shape
+    M = batch * seq_len
+    y, hc, hl = _scan_outputs(u, batch, seq_len, D, N, out, h_cache, h_last)
+    dims = make_dims(batch, seq_len, D, N, 1)
+    _check("mss_selective_scan", lib().mss_selective_scan(
+        ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
+        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
+        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
+        _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
+        _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+        _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
+    return y, hc, hl
+
+
+def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
+                seq_len, disc, h_cache=False, h_last=False, out=None, stream=None):
+    """Fused conv1d + SiLU + selective scan + gate from x.  Returns (y, h_cache, h_last)."""
+    D, N = A_log.shape
+    K = w_conv.shape[1]
+    M = batch * seq_len
+    y, hc, hl = _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last)
+    dims = make_dims(batch, seq_len, D, N, K)
+    _check("mss_mamba1_core", lib().mss_mamba1_core(
+        ctypes.byref(dims), _disc(disc), _ptr(x, "x", (M, D)), _ptr(w_conv, "w_conv", (D, K)),
+        _ptr(b_conv, "b_conv", (D,), False), _ptr(delta, "delta", (M, D)),
+        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
+        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
+        _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
+        _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+        _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
+    return y, hc, hl
+
+
+def selective_step(x, z, delta, A_log, B, C, D_vec, w_conv, b_conv, conv_state, h, *, disc,
+                   out=None, stream=None):
+    """One decode step; updates ``conv_state`` and ``h`` in place.  Returns y (batch, D)."""
+    batch, D = x.shape
+    N = A_log.shape[1]
+    K = w_conv.shape[1]
+    y = out if out is not None else _empty((batch, D), x)
+    dims = make_dims(batch, 1, D, N, K)
+    _check("mss_selective_step", lib().mss_selective_step(
+        ctypes.byref(dims), _disc(disc), _ptr(x, "x", (batch, D)),
+        _ptr(z, "z", (batch, D), False), _ptr(delta, "delta", (batch, D)),
+        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (batch, N)), _ptr(C, "C", (batch, N)),
+        _ptr(D_vec, "D_vec", (D,), False), _ptr(w_conv, "w_conv", (D, K)),
+        _ptr(b_conv, "b_conv", (D,), False),
+        _ptr(conv_state, "conv_state", (batch, K - 1, D), K > 1),
+        _ptr(h, "h", (batch, D, N)), _ptr(y, "y", (batch, D)), _stream(stream)))
+    return y

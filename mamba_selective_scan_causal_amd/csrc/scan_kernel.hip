@@ -1,0 +1,435 @@
+// scan_kernel.hip -- selective scan (optionally fused with the causal conv1d +
+// SiLU that produces its input) for gfx950.
+//
+// Computes mamba1CpuForward steps 4-5 (fused variant only), 8 and 9 of the
+// Mamba-1 CPU mirror (builderforce-memory-engine 2026.7.12 -> 2026.9.27,
+// src/training/mamba1_cpu.ts): per (b, d) column and time step t
+//   u  = SiLU(bConv + sum_k wConv[d,k] x[t-k])      (fused variant; else u given)
+//   dv = softplus(delta),  aBar_n = exp(dv * A_n)
+//   h_n = aBar_n h_n + bBar_n u,   y = D u + sum_n C_n h_n,   out = y SiLU(z)
+//
+// Mapping.  One wave64 per work item; lane = channel d, so each lane owns the
+// full N-state vector of its column in VGPRs and the N-reduction for y stays
+// inside the lane.  Time advances in straight-line blocks of kT steps: at the
+// start of a block the wave issues the loads of the next block (one 256-byte
+// row segment per tensor and step, addressed as a uniform row base plus a
+// 32-bit lane offset) and fetches the next block's B and C rows (1 KB, one
+// 16-byte load per lane), which it stages through LDS; every step then reads
+// its B_t / C_t with broadcast LDS loads, which cost no VALU issue slots.
+// The path is VALU-bound (one v_exp_f32 per (t, d, n) at half the FMA rate
+// plus ~4 FMA-class operations), so the per-step arithmetic is kept minimal.
+//
+// Parallelism over time.  The B * ceil(D/64) column tiles alone give too few
+// waves for 1024 SIMDs, so the flattened (tile, t) space is cut into equal
+// segments, one per wave.  A segment that starts at t0 > 0 needs the state
+// h(t0 - 1).  Because the recurrence forgets exponentially -- the part of
+// h(t0-1) that comes from before step s is multiplied by
+// prod_{r=s}^{t0-1} aBar_r = exp(A_n * sum_r dv_r) -- the wave first walks
+// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= 30 ln 2 holds in
+// every lane (or t = 0 is reached), then replays the recurrence forward from
+// that step with h = 0 (state only, no outputs).  What this drops is exactly
+// the state at the replay start times a factor <= 2^-30 per state; reaching
+// t = 0 makes it exact.  No workspace and no inter-wave synchronisation.
+#include "device_math.h"
+#include "launch.h"
+
+namespace mss {
+namespace {
+
+constexpr int kT = 8;                         // steps per straight-line block
+constexpr int kBackBlk = 16;                  // delta loads in flight in the backward walk
+constexpr float kDecayCut = 30.0f;            // replay until the carried part decays by 2^-30
+// Below |dv*A| = 2^-6 the decay is applied through expm1 (see step()).
+constexpr float kSmallX = 0.015625f;
+constexpr float kSmallX2 = kSmallX * kLog2e;  // the same bound in log2 units
+
+struct Cols {
+    const float* __restrict__ src;      // x (fused) or u, (M, D)
+    const float* __restrict__ delta;    // (M, D)
+    const float* __restrict__ A_log;    // (D, N)
+    const float* __restrict__ Bm;       // (M, N)
+    const float* __restrict__ Cm;       // (M, N)
+    const float* __restrict__ Dv;       // (D) or null
+    const float* __restrict__ z;        // (M, D) or null
+    const float* __restrict__ h0;       // (B, D, N) or null
+    const float* __restrict__ w_conv;   // (D, K) fused only
+    const float* __restrict__ b_conv;   // (D) or null
+    float* __restrict__ y;              // (M, D)
+    float* __restrict__ h_cache;        // (B, L, D, N) or null
+    float* __restrict__ h_last;         // (B, D, N) or null
+};
+
+// Per-lane constants and state of one (b, d) column.
+template <int KS, int NS>
+struct Lane {
+    static constexpr int NR = NS > 0 ? NS : kMaxN;                   // register slots for states
+    static constexpr int KR = KS > 0 ? KS : (KS == 0 ? kMaxK : 1);  // conv taps held
+    float A2[NR];       // A * log2(e)
+    float Ai[NR];       // 1 / A (ZOH only)
+    float h[NR];
+    float w[KR];
+    float xw[KR > 1 ? KR - 1 : 1];  // xw[j] = conv input at t-1-j
+    float bias, dvec, min_a2;
+};
+
+// Output modes of a sweep.
+constexpr int kWarm = 0;     // state only
+constexpr int kOut = 1;      // y
+constexpr int kOutHC = 2;    // y and hCache
+
+template <int DISC, int KS, int NS>
+struct Scan {
+    using L_t = Lane<KS, NS>;
+    static constexpr int NR = L_t::NR;
+    static constexpr int KR = L_t::KR;
+    static constexpr bool kFused = KS >= 0;
+    static constexpr bool kStage = NS == 16;   // B/C rows staged through LDS
+
+    const Cols& c;
+    const int64_t L, D;
+    const int N, K;
+    const uint32_t d;       // this lane's channel, clamped to D-1
+    const int64_t b;
+    const float* zsrc;      // z, or any valid array when ungated
+    const bool gated;
+    float4* lds;            // 64 float4 for this wave: B rows [0, 32), C rows [32, 64)
+
+    // Lanes past D compute channel D-1 again and store bit-identical values to
+    // the same addresses as lane D-1, so no store needs a lane mask.
+    __device__ Scan(const Cols& c_, const ScanShape& s, int64_t b_, int64_t d_raw, float4* lds_)
+        : c(c_), L(s.L), D(s.D), N(NS > 0 ? NS : s.N), K(KS > 0 ? KS : s.K),
+          d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)), b(b_),
+          zsrc(c_.z ? c_.z : c_.src), gated(c_.z != nullptr), lds(lds_) {}
+
+    __device__ __forceinline__ int64_t row(int64_t t) const { return b * L + t; }
+    __device__ __forceinline__ float ld(const float* base, int64_t t) const {
+        return (base + row(t) * D)[d];
+    }
+
+    __device__ __forceinline__ void init(L_t& ln) const {
+        float mn = 3.0e38f;
+#pragma unroll
+        for (int n = 0; n < NR; n++) {
+            if (NS > 0 || n < N) {
+                const float A = a_cont(c.A_log[d * N + n]);
+                ln.A2[n] = A * kLog2e;
+                ln.Ai[n] = 1.0f / A;
+                mn = __builtin_fminf(mn, -ln.A2[n]);
+            } else {            // padding state: never fed, never read
+                ln.A2[n] = -1.0f;
+                ln.Ai[n] = 0.0f;
+            }
+            ln.h[n] = 0.0f;
+        }
+        ln.min_a2 = mn;
+        ln.dvec = c.Dv ? c.Dv[d] : 0.0f;
+        if constexpr (kFused) {
+            ln.bias = c.b_conv ? c.b_conv[d] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < KR; k++) ln.w[k] = (KS > 0 || k < K) ? c.w_conv[d * K + k] : 0.0f;
+        }
+    }
+
+    // First step of the forward replay: pick it by walking delta backwards.
+    __device__ __forceinline__ int64_t replay_start(const L_t& ln, int64_t t0) const {
+        if (t0 == 0) return 0;
+        float S = 0.0f;
+        int64_t t = t0;  // next step to visit is t - 1
+        while (true) {
+            float dd[kBackBlk];
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t - 1 - i;
+                dd[i] = ld(c.delta, tt >= 0 ? tt : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t - 1 - i;
+                if (tt < 0) return 0;
+                S += softplus(dd[i]);
+                if (wave_all(S * ln.min_a2 >= kDecayCut)) return tt;
+            }
+            t -= kBackBlk;
+        }
+    }
+
+    __device__ __forceinline__ void load_window(L_t& ln, int64_t t) const {
+        if constexpr (kFused) {
+#pragma unroll
+            for (int j = 0; j < KR - 1; j++) {
+                const int64_t tt = t - 1 - j;
+                ln.xw[j] = (j < K - 1 && tt >= 0) ? ld(c.src, tt) : 0.0f;
+            }
+        }
+    }
+
+    // Inputs of steps t0 .. t0+kT-1 (rows past the sequence end are clamped
+    // to its last row; they are never used).
+    template <int OUT>
+    __device__ __forceinline__ void load_block(float (&xs)[kT], float (&ds)[kT], float (&zs)[kT],
+                                               int64_t t0) const {
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            const int64_t t = t0 + i < L ? t0 + i : L - 1;
+            xs[i] = ld(c.src, t);
+            ds[i] = ld(c.delta, t);
+            if constexpr (OUT != kWarm) zs[i] = ld(zsrc, t);
+        }
+    }
+
+    // This lane's 16 bytes of the B rows (lanes 0-31) or C rows (lanes 32-63)
+    // of steps t0 .. t0+kT-1.
+    __device__ __forceinline__ float4 load_bc(int64_t t0) const {
+        const uint32_t lane = threadIdx.x;
+        const uint32_t q = lane & 31u;
+        int64_t t = t0 + (q >> 2);
+        t = t < L ? t : L - 1;
+        const float* base = lane < 32 ? c.Bm : c.Cm;
+        return *reinterpret_cast<const float4*>(base + row(t) * 16 + (q & 3u) * 4);
+    }
+
+    // One time step.  SLOW: some lane has |dv A| < 2^-6 (see below).
+    // LDS: B_t / C_t come from the staged block at row i; otherwise from
+    // scalar loads.
+    template <int OUT, bool SLOW, bool LDS>
+    __device__ __forceinline__ void step(L_t& ln, float xv, float dv, float zv, int64_t t,
+                                         int i) const {
+        float u;
+        if constexpr (kFused) {
+            float acc = __builtin_fmaf(ln.w[0], xv, ln.bias);
+#pragma unroll
+            for (int k = 1; k < KR; k++)
+                if (KS > 0 || k < K) acc = __builtin_fmaf(ln.w[k], ln.xw[k - 1], acc);
+#pragma unroll
+            for (int j = KR - 2; j > 0; j--) ln.xw[j] = ln.xw[j - 1];
+            if constexpr (KR > 1) ln.xw[0] = xv;
+            u = silu(acc);
+        } else {
+            u = xv;
+        }
+        float Bv[NR], Cv[NR];
+        if constexpr (LDS) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4 bq = lds[i * 4 + q];
+                Bv[4 * q] = bq.x; Bv[4 * q + 1] = bq.y; Bv[4 * q + 2] = bq.z; Bv[4 * q + 3] = bq.w;
+                if constexpr (OUT != kWarm) {
+                    const float4 cq = lds[32 + i * 4 + q];
+                    Cv[4 * q] = cq.x; Cv[4 * q + 1] = cq.y; Cv[4 * q + 2] = cq.z; Cv[4 * q + 3] = cq.w;
+                }
+            }
+        } else {
+            const cfloat* Br = as_const(c.Bm + row(t) * N);
+            const cfloat* Cr = as_const(c.Cm + row(t) * N);
+#pragma unroll
+            for (int n = 0; n < NR; n++) {
+                Bv[n] = (NS > 0 || n < N) ? Br[n] : 0.0f;
+                if constexpr (OUT != kWarm) Cv[n] = (NS > 0 || n < N) ? Cr[n] : 0.0f;
+            }
+        }
+        float yv = ln.dvec * u;
+        if constexpr (!SLOW) {
+            // |dv * A| >= 2^-6 in every lane and state: aBar <= 0.985, the
+            // memory is short and aBar is used directly.
+            if constexpr (DISC == MSS_DISC_EULER) {
+                const float dvu = dv * u;
+#pragma unroll
+                for (int n = 0; n < NR; n++) {
+                    if (NS > 0 || n < N) {
+                        const float a = ex2(dv * ln.A2[n]);
+                        ln.h[n] = __builtin_fmaf(a, ln.h[n], dvu * Bv[n]);
+                        if constexpr (OUT != kWarm) yv = __builtin_fmaf(Cv[n], ln.h[n], yv);
+                    }
+                }
+            } else {
+                // h' = aBar (h + K) - K with K = u B / A  (= aBar h + (aBar - 1) K)
+#pragma unroll
+                for (int n = 0; n < NR; n++) {
+                    if (NS > 0 || n < N) {
+                        const float a = ex2(dv * ln.A2[n]);
+                        const float k = (u * ln.Ai[n]) * Bv[n];
+                        ln.h[n] = __builtin_fmaf(a, ln.h[n] + k, -k);
+                        if constexpr (OUT != kWarm) yv = __builtin_fmaf(Cv[n], ln.h[n], yv);
+                    }
+                }
+            }
+        } else {
+            // Some lane has a nearly-integrating state.  Carry the decay as
+            // h + m h with m = aBar - 1 = expm1(dv A): fl(aBar) near 1 has an
+            // absolute error of ~3e-8 that would compound over the long memory,
+            // m has a relative one.  m is a cubic when |dv A| < 2^-6
+            // (truncation < 2e-7 relative), else aBar - 1.
+            const float dvu = dv * u;
+#pragma unroll
+            for (int n = 0; n < NR; n++) {
+                if (NS > 0 || n < N) {
+                    const float x2 = dv * ln.A2[n];
+                    const float a = ex2(x2);
+                    const float x = x2 * kLn2;
+                    const float p = x * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 6.0f, 0.5f), 1.0f);
+                    const float m = __builtin_fabsf(x) < kSmallX ? p : a - 1.0f;
+                    if constexpr (DISC == MSS_DISC_EULER) {
+                        ln.h[n] = __builtin_fmaf(dvu, Bv[n], __builtin_fmaf(m, ln.h[n], ln.h[n]));
+                    } else {
+                        const float k = (u * ln.Ai[n]) * Bv[n];
+                        ln.h[n] = __builtin_fmaf(m, ln.h[n] + k, ln.h[n]);
+                    }
+                    if constexpr (OUT != kWarm) yv = __builtin_fmaf(Cv[n], ln.h[n], yv);
+                }
+            }
+        }
+        if constexpr (OUT != kWarm) {
+            const int64_t r = row(t);
+            const float g = silu(zv);
+            (c.y + r * D)[d] = gated ? yv * g : yv;
+            if constexpr (OUT == kOutHC) {
+                float* __restrict__ hc = c.h_cache + r * D * N;
+                if constexpr (NS > 0 && NS % 4 == 0) {
+#pragma unroll
+                    for (int n = 0; n < NR; n += 4)
+                        *reinterpret_cast<float4*>(hc + d * NS + n) =
+                            make_float4(ln.h[n], ln.h[n + 1], ln.h[n + 2], ln.h[n + 3]);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NR; n++)
+                        if (n < N) hc[d * N + n] = ln.h[n];
+                }
+            }
+        }
+    }
+
+    // Steps t0 .. t0+cnt-1 one at a time (not unrolled): loads its own
+    // inputs and makes the fast/slow choice per step.  Used for the slow
+    // path, block remainders, the hCache mode and B/C without LDS staging.
+    // LDS: the block's B/C rows are staged (step i of the block at row i).
+    template <int OUT, bool LDS>
+    __device__ __forceinline__ void steps1(L_t& ln, int64_t t0, int cnt) const {
+        for (int i = 0; i < cnt; i++) {
+            const int64_t t = t0 + i;
+            const float xv = ld(c.src, t);
+            const float dv = softplus(ld(c.delta, t));
+            const float zv = OUT != kWarm ? ld(zsrc, t) : 0.0f;
+            if (!wave_any(dv * ln.min_a2 < kSmallX2))
+                step<OUT, false, LDS>(ln, xv, dv, zv, t, i);
+            else
+                step<OUT, true, LDS>(ln, xv, dv, zv, t, i);
+        }
+    }
+
+    // Steps [tb, te) of one sweep.  Full blocks of kT steps whose every lane
+    // is on the fast path run as straight-line code on prefetched inputs;
+    // other blocks and the remainder go through steps1.
+    template <int OUT>
+    __device__ __forceinline__ void sweep(L_t& ln, int64_t tb, int64_t te) const {
+        if (tb >= te) return;
+        if constexpr (!kStage || OUT == kOutHC) {
+            for (int64_t t = tb; t < te; t += kT) {
+                const int cnt = te - t < kT ? static_cast<int>(te - t) : kT;
+                if constexpr (kStage) lds[threadIdx.x] = load_bc(t);
+                steps1<OUT, kStage>(ln, t, cnt);
+            }
+        } else {
+            float nx[kT], nd[kT], nz[kT];
+            float4 nbc = load_bc(tb);
+            load_block<OUT>(nx, nd, nz, tb);
+            int64_t t = tb;
+            for (; t + kT <= te; t += kT) {
+                float cx[kT], cz[kT], dv[kT];
+                bool small = false;
+#pragma unroll
+                for (int i = 0; i < kT; i++) {
+                    cx[i] = nx[i];
+                    cz[i] = nz[i];
+                    dv[i] = softplus(nd[i]);
+                    small = small || (dv[i] * ln.min_a2 < kSmallX2);
+                }
+                lds[threadIdx.x] = nbc;
+                load_block<OUT>(nx, nd, nz, t + kT);
+                nbc = load_bc(t + kT);
+                if (!wave_any(small)) {
+#pragma unroll
+                    for (int i = 0; i < kT; i++) step<OUT, false, true>(ln, cx[i], dv[i], cz[i], t + i, i);
+                } else {
+                    steps1<OUT, true>(ln, t, kT);
+                }
+            }
+            if (t < te) {
+                lds[threadIdx.x] = nbc;
+                steps1<OUT, true>(ln, t, static_cast<int>(te - t));
+            }
+        }
+    }
+
+    // Produce outputs for steps [t0, t1) of this column.
+    __device__ __forceinline__ void run(int64_t t0, int64_t t1) const {
+        L_t ln;
+        init(ln);
+        const int64_t tw = replay_start(ln, t0);
+        if (tw == 0 && c.h0) {
+#pragma unroll
+            for (int n = 0; n < NR; n++)
+                if (NS > 0 || n < N) ln.h[n] = c.h0[(b * D + d) * N + n];
+        }
+        load_window(ln, tw);
+        sweep<kWarm>(ln, tw, t0);
+        if (c.h_cache)
+            sweep<kOutHC>(ln, t0, t1);
+        else
+            sweep<kOut>(ln, t0, t1);
+        if (t1 == L && c.h_last) {
+#pragma unroll
+            for (int n = 0; n < NR; n++)
+                if (NS > 0 || n < N) c.h_last[(b * D + d) * N + n] = ln.h[n];
+        }
+    }
+};
+
+template <int DISC, int KS, int NS>
+__global__ __launch_bounds__(kWave) void scan_kernel(Cols c, ScanShape s) {
+    __shared__ float4 lds[kWave];
+    const int64_t lane = threadIdx.x;
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * s.seg;
+    const int64_t g1 = g0 + s.seg < s.total ? g0 + s.seg : s.total;
+    // A segment of the flattened (tile, t) space may cover the end of one
+    // tile and the start of the next; walk its pieces.
+    for (int64_t g = g0; g < g1;) {
+        const int64_t tile = g / s.L;
+        const int64_t t0 = g - tile * s.L;
+        const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
+        const int64_t b = tile / s.tiles_per_b;
+        const int64_t dt = tile - b * s.tiles_per_b;
+        Scan<DISC, KS, NS> sc(c, s, b, dt * kWave + lane, lds);
+        sc.run(t0, t1);
+        g += t1 - t0;
+    }
+}
+
+template <int DISC, int KS, int NS>
+hipError_t launch_t(const Cols& c, const ScanShape& s, hipStream_t st) {
+    const int64_t nblk = (s.total + s.seg - 1) / s.seg;
+    hipLaunchKernelGGL((scan_kernel<DISC, KS, NS>), dim3(static_cast<unsigned>(nblk)),
+                       dim3(kWave), 0, st, c, s);
+    return hipGetLastError();
+}
+
+template <int DISC, int KS>
+hipError_t launch_n(const Cols& c, const ScanShape& s, hipStream_t st) {
+    return s.N == 16 ? launch_t<DISC, KS, 16>(c, s, st) : launch_t<DISC, KS, 0>(c, s, st);
+}
+
+template <int DISC>
+hipError_t launch_k(const Cols& c, const ScanShape& s, hipStream_t st, bool fused) {
+    if (!fused) return launch_n<DISC, -1>(c, s, st);
+    return s.K == 4 ? launch_n<DISC, 4>(c, s, st) : launch_n<DISC, 0>(c, s, st);
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanArgs& a, const ScanShape& s, hipStream_t st) {
+    Cols c{a.src, a.delta, a.A_log, a.B, a.C, a.D_vec, a.z, a.h0, a.w_conv, a.b_conv,
+           a.y, a.h_cache, a.h_last};
+    return a.disc == MSS_DISC_EULER ? launch_k<MSS_DISC_EULER>(c, s, st, a.fused)
+                                    : launch_k<MSS_DISC_ZOH>(c, s, st, a.fused);
+}
+
+}  // namespace mss

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mss.h declares, and rejects bad arguments before any launch.
+
+Pointers here are fake aligned integers: validation never dereferences them,
+and every call below fails (or is empty) before reaching a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_causal_amd as mss
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mss.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mss_\w+)\s*\(", text, re.M)))
+
+
+def header_define(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mss.lib()
+
+
+def test_exports_every_declared_function(L):
+    fns = header_functions()
+    assert set(fns) == set(mss.EXPORTS), fns
+    for f in fns:
+        assert hasattr(L, f), f"{f} not exported"
+
+
+def test_version_and_strerror(L):
+    assert L.mss_version() == header_define("MSS_VERSION")
+    for name in ("MSS_OK", "MSS_EINVAL", "MSS_EALIGN", "MSS_EALIAS", "MSS_EHIP"):
+        s = L.mss_strerror(header_define(name))
+        assert s and s != b"unknown status"
+    assert L.mss_strerror(12345) == b"unknown status"
+    assert ctypes.sizeof(mss.Dims) == 48
+
+
+EINVAL, EALIGN, EALIAS = (header_define(n) for n in ("MSS_EINVAL", "MSS_EALIGN", "MSS_EALIAS"))
+BASE = 0x7F0000000000
+
+
+def fake(i, nbytes=1 << 20):
+    """Distinct, 16-byte aligned, non-overlapping fake device addresses."""
+    return ctypes.c_void_p(BASE + i * (1 << 32))
+
+
+def scan_call(L, dims, disc=0, **over):
+    args = dict(u=fake(1), delta=fake(2), A_log=fake(3), B=fake(4), C=fake(5), D_vec=fake(6),
+                z=fake(7), h0=None, y=fake(8), h_cache=None, h_last=None)
+    args.update(over)
+    return L.mss_selective_scan(ctypes.byref(dims), disc, *args.values(), None)
+
+
+def test_scan_validation(L):
+    d = mss.make_dims(2, 16, 64, 16, 4)
+    assert L.mss_selective_scan(None, 0, *([None] * 11), None) == EINVAL
+    bad = mss.make_dims(2, 16, 64, 16, 4)
+    bad.struct_size = 40
+    assert scan_call(L, bad) == EINVAL
+    bad = mss.make_dims(2, 16, 64, 16, 4)
+    bad.reserved = 1
+    assert scan_call(L, bad) == EINVAL
+    assert scan_call(L, mss.make_dims(2, 16, 64, 17, 4)) == EINVAL       # N > 16
+    assert scan_call(L, mss.make_dims(2, 16, 64, 0, 4)) == EINVAL        # N < 1
+    assert scan_call(L, mss.make_dims(-1, 16, 64, 16, 4)) == EINVAL      # negative size
+    assert scan_call(L, d, disc=2) == EINVAL                              # disc has no default
+    assert scan_call(L, d, u=None) == EINVAL                              # required tensor
+    assert scan_call(L, d, C=None) == EINVAL
+    assert scan_call(L, d, delta=ctypes.c_void_p(BASE + 4)) == EALIGN
+    assert scan_call(L, d, y=fake(1)) == EALIAS                           # y == u
+    assert scan_call(L, d, y=ctypes.c_void_p(BASE + 2 * (1 << 32) + 256)) == EALIAS  # y inside delta
+    assert scan_call(L, d, h_last=fake(8)) == EALIAS                      # two outputs overlap
+    huge = mss.make_dims(1 << 40, 1 << 20, 1 << 20, 16, 4)
+    assert scan_call(L, huge) == EINVAL                                   # overflowing sizes
+
+
+def test_empty_problems_launch_nothing(L):
+    # zero channels: nothing to compute; only B and C (M, N) still hold elements
+    dims = mss.make_dims(2, 16, 0, 16, 4)
+    assert L.mss_selective_scan(ctypes.byref(dims), 0, *([None] * 11), None) == EINVAL
+    scan = [None] * 11
+    scan[3], scan[4] = fake(4), fake(5)
+    assert L.mss_selective_scan(ctypes.byref(dims), 0, *scan, None) == 0
+    core = [None] * 13
+    core[5], core[6] = fake(4), fake(5)
+    assert L.mss_mamba1_core(ctypes.byref(dims), 1, *core, None) == 0
+    assert L.mss_conv1d_silu(ctypes.byref(dims), None, None, None, None, None) == 0
+    step = [None] * 12
+    step[4], step[5] = fake(4), fake(5)
+    assert L.mss_selective_step(ctypes.byref(dims), 0, *step, None) == 0
+    # zero batch: the per-channel parameters still hold elements and are required
+    dims = mss.make_dims(0, 16, 64, 16, 4)
+    assert L.mss_selective_scan(ctypes.byref(dims), 0, *([None] * 11), None) == EINVAL
+    assert L.mss_selective_scan(ctypes.byref(dims), 0, None, None, fake(3), *([None] * 8),
+                                None) == 0
+    core = [None] * 13
+    core[1], core[4] = fake(2), fake(3)   # w_conv, A_log
+    assert L.mss_mamba1_core(ctypes.byref(dims), 1, *core, None) == 0
+    assert L.mss_conv1d_silu(ctypes.byref(dims), None, fake(2), None, None, None) == 0
+    step = [None] * 12
+    step[3], step[7] = fake(3), fake(4)   # A_log, w_conv
+    assert L.mss_selective_step(ctypes.byref(dims), 0, *step, None) == 0
+    # seq_len 0 without h_last: nothing to launch
+    dims = mss.make_dims(2, 0, 64, 16, 4)
+    assert L.mss_selective_scan(ctypes.byref(dims), 0, None, None, fake(3), None, None, None, None,
+                                None, None, None, None, None) == 0
+
+
+def test_core_and_conv_validation(L):
+    d = mss.make_dims(2, 16, 64, 16, 9)  # K > 8
+    assert L.mss_conv1d_silu(ctypes.byref(d), fake(1), fake(2), None, fake(3), None) == EINVAL
+    d = mss.make_dims(2, 16, 64, 16, 4)
+    assert L.mss_conv1d_silu(ctypes.byref(d), fake(1), fake(2), None, fake(1), None) == EALIAS
+    assert L.mss_conv1d_silu(ctypes.byref(d), fake(1), None, None, fake(3), None) == EINVAL
+    args = [fake(i) for i in range(1, 14)]
+    args[1] = None  # w_conv missing
+    assert L.mss_mamba1_core(ctypes.byref(d), 0, *args, None) == EINVAL
+    d0 = mss.make_dims(2, 16, 64, 16, 0)  # K = 0
+    assert L.mss_mamba1_core(ctypes.byref(d0), 0, *[fake(i) for i in range(1, 14)], None) == EINVAL
+
+
+def test_step_validation(L):
+    d = mss.make_dims(4, 1, 64, 16, 4)
+    args = [fake(i) for i in range(1, 13)]  # x z delta A_log B C D_vec w b conv_state h y
+    a = list(args)
+    a[9] = None  # conv_state required when K > 1
+    assert L.mss_selective_step(ctypes.byref(d), 0, *a, None) == EINVAL
+    a = list(args)
+    a[11] = a[0]  # y == x
+    assert L.mss_selective_step(ctypes.byref(d), 0, *a, None) == EALIAS
+    a = list(args)
+    a[10] = ctypes.c_void_p(BASE + 8)
+    assert L.mss_selective_step(ctypes.byref(d), 0, *a, None) == EALIGN
+    assert L.mss_selective_step(ctypes.byref(d), 5, *args, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mss, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mss, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        mss.lib()

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on
+the same seeded inputs, within max relative error 1e-4 (see gpu_util.rel_err).
+
+Every output buffer is pre-filled with NaN, so an element a kernel fails to
+write shows up as an infinite error."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import mamba_selective_scan_causal_amd as mss
+from mamba_selective_scan_causal_amd import inputs as gen
+from gpu_util import announce, assert_close, dev, host, nan_like
+
+pytestmark = pytest.mark.gpu
+
+DISCS = ("zoh", "euler")
+FULL = [gen.TINY_CLAMP, gen.SMALL, gen.MAMBA_130M]
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    announce(request.node.nodeid)
+    yield
+
+
+def run_core(inp, w, disc, *, h0=None, h_cache=None, h_last=True, gated=True, dvec=True):
+    B, L, D, N = w.batch, w.seq_len, w.d_inner, w.d_state
+    d = {k: dev(v) for k, v in inp.items()}
+    y = nan_like((B * L, D))
+    hc = nan_like((B, L, D, N)) if (w.hcache if h_cache is None else h_cache) else False
+    hl = nan_like((B, D, N)) if h_last else False
+    mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                    d["D_vec"] if dvec else None, d["z"] if gated else None,
+                    dev(h0) if h0 is not None else None, batch=B, seq_len=L, disc=disc,
+                    h_cache=hc, h_last=hl, out=y)
+    import torch
+    torch.cuda.synchronize()
+    return (host(y), host(hc) if hc is not False else None, host(hl) if hl is not False else None)
+
+
+def oracle_core(inp, w, disc, *, h0=None, h_cache=None, gated=True, dvec=True, cols=None):
+    return oracle.mamba1_core(inp["x"], inp["w_conv"], inp["b_conv"], inp["delta"], inp["A_log"],
+                              inp["B"], inp["C"], inp["D_vec"] if dvec else None,
+                              inp["z"] if gated else None, h0, batch=w.batch, seq_len=w.seq_len,
+                              disc=disc, cols=cols,
+                              h_cache=(w.hcache if h_cache is None else h_cache) and cols is None,
+                              h_last=True)
+
+
+# ---------------------------------------------------------------------------
+# the workloads, in full
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_conv1d_silu(w):
+    inp = gen.generate(w)
+    B, L, D = w.batch, w.seq_len, w.d_inner
+    u = nan_like((B * L, D))
+    mss.conv1d_silu(dev(inp["x"]), dev(inp["w_conv"]), dev(inp["b_conv"]), batch=B, seq_len=L,
+                    out=u)
+    want = oracle.conv1d_silu(inp["x"], inp["w_conv"], inp["b_conv"], batch=B, seq_len=L)
+    assert_close(host(u), want, "u")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_core_full(w, disc):
+    inp = gen.generate(w)
+    y, hc, hl = run_core(inp, w, disc)
+    oy, ohc, ohl = oracle_core(inp, w, disc)
+    assert_close(y, oy, "y")
+    assert_close(hl, ohl, "h_last")
+    if w.hcache:
+        assert_close(hc, ohc, "h_cache")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("w", [gen.TINY_CLAMP, gen.SMALL], ids=lambda w: w.name)
+def test_scan_on_given_u(w, disc):
+    inp = gen.generate(w)
+    B, L, D, N = w.batch, w.seq_len, w.d_inner, w.d_state
+    u = inp["x"]  # any fp32 tensor serves as u
+    d = {k: dev(v) for k, v in inp.items()}
+    y, hc, hl = nan_like((B * L, D)), nan_like((B, L, D, N)), nan_like((B, D, N))
+    mss.selective_scan(dev(u), d["delta"], d["A_log"], d["B"], d["C"], d["D_vec"], d["z"], None,
+                       batch=B, seq_len=L, disc=disc, h_cache=hc, h_last=hl, out=y)
+    oy, ohc, ohl = oracle.selective_scan(u, inp["delta"], inp["A_log"], inp["B"], inp["C"],
+                                         inp["D_vec"], inp["z"], None, batch=B, seq_len=L,
+                                         disc=disc, h_cache=True, h_last=True)
+    assert_close(host(y), oy, "y")
+    assert_close(host(hc), ohc, "h_cache")
+    assert_close(host(hl), ohl, "h_last")
+
+
+def _sample_cols(B, D, rng, per_b=24):
+    cols = []
+    for b in range(B):
+        ds = {0, 1, 63, 64, D // 2, D - 2, D - 1} | set(rng.integers(0, D, per_b).tolist())
+        cols += [b * D + d for d in sorted(ds) if 0 <= d < D]
+    return np.array(cols, dtype=np.int64)
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_core_2p8b_width_sampled(disc):
+    """The 4 x 8192 x 5120 workload at full size in the benchmark's launch
+    configuration; the oracle recomputes whole sampled (b, d) columns."""
+    import torch
+    w = gen.MAMBA_2P8B
+    inp = gen.generate(w)
+    B, L, D = w.batch, w.seq_len, w.d_inner
+    d = {k: dev(v) for k, v in inp.items()}
+    y = nan_like((B * L, D))
+    hl = nan_like((B, D, w.d_state))
+    mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                    d["D_vec"], d["z"], None, batch=B, seq_len=L, disc=disc, h_last=hl, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item(), "unwritten output elements"
+    cols = _sample_cols(B, D, np.random.default_rng(3))
+    bs = torch.as_tensor(cols // D, device="cuda")
+    ds = torch.as_tensor(cols % D, device="cuda")
+    got = host(y.view(B, L, D)[bs, :, ds])
+    oy, _, ohl = oracle_core(inp, w, disc, cols=cols)
+    assert_close(got, oy, "y (sampled columns)")
+    assert_close(host(hl.view(B * D, -1)[torch.as_tensor(cols, device="cuda")]), ohl,
+                 "h_last (sampled)")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_decode_64_steps_sampled(disc):
+    """256 sequences x 5120 channels, 64 consecutive single-token steps from a
+    random carried state; the oracle chains the same steps on sampled columns."""
+    import torch
+    w = gen.DECODE
+    inp = gen.generate(w)
+    S, B, D, N, K = w.seq_len, w.batch, w.d_inner, w.d_state, w.d_conv
+    cols = _sample_cols(B, D, np.random.default_rng(4), per_b=2)[::3]
+    ccols = torch.as_tensor(cols, device="cuda")
+    d = {k: dev(v) for k, v in inp.items()}
+    h = d["h"].clone()
+    cs = d["conv_state"].clone()
+    o_h = inp["h"].reshape(B * D, N)[cols].astype(np.float64)
+    o_cs = inp["conv_state"].transpose(0, 2, 1).reshape(B * D, K - 1)[cols].astype(np.float64)
+    y = nan_like((B, D))
+    for s in range(S):
+        y.fill_(float("nan"))
+        mss.selective_step(d["x"][s], d["z"][s], d["delta"][s], d["A_log"], d["B"][s], d["C"][s],
+                           d["D_vec"], d["w_conv"], d["b_conv"], cs, h, disc=disc, out=y)
+        oy, o_cs, o_h = oracle.selective_step(inp["x"][s], inp["z"][s], inp["delta"][s],
+                                              inp["A_log"], inp["B"][s], inp["C"][s],
+                                              inp["D_vec"], inp["w_conv"], inp["b_conv"], o_cs,
+                                              o_h, disc=disc, cols=cols)
+        assert_close(host(y.view(-1)[ccols]), oy, f"y step {s}")
+        assert not torch.isnan(y).any().item()
+    assert_close(host(h.view(B * D, N)[ccols]), o_h, "h after 64 steps")
+    got_cs = host(cs.permute(0, 2, 1).reshape(B * D, K - 1)[ccols])
+    assert np.array_equal(got_cs, o_cs), "conv state after 64 steps"
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+
+
+EDGE = [
+    # (name, overrides)
+    ("ragged_d", dict(batch=3, seq_len=777, d_inner=100)),
+    ("many_segments_one_tile", dict(batch=1, seq_len=4096, d_inner=64)),
+    ("segments_cross_tiles", dict(batch=2, seq_len=3001, d_inner=130)),
+    ("len1", dict(batch=2, seq_len=1, d_inner=70)),
+    ("len_below_k", dict(batch=2, seq_len=2, d_inner=64)),
+    ("n8", dict(batch=2, seq_len=300, d_inner=96, d_state=8)),
+    ("n5", dict(batch=2, seq_len=300, d_inner=96, d_state=5)),
+    ("n1", dict(batch=1, seq_len=200, d_inner=64, d_state=1)),
+    ("k1", dict(batch=2, seq_len=300, d_inner=64, d_conv=1)),
+    ("k2", dict(batch=2, seq_len=300, d_inner=64, d_conv=2)),
+    ("k3", dict(batch=2, seq_len=300, d_inner=64, d_conv=3)),
+    ("k8", dict(batch=2, seq_len=300, d_inner=64, d_conv=8)),
+    ("bias", dict(batch=2, seq_len=500, d_inner=128, b_conv="normal")),
+    ("slow_decay_full_replay", dict(batch=2, seq_len=3000, d_inner=64, alog_clamp_frac=1.0)),
+    ("tiny_steps", dict(batch=2, seq_len=1500, d_inner=64, delta_mean=-9.0, delta_var=1.0)),
+]
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("name,over", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, over, disc):
+    w = gen.SMALL.with_(name=name, hcache=over.get("seq_len", 0) <= 1000, **over)
+    inp = gen.generate(w, seed_offset=7)
+    y, hc, hl = run_core(inp, w, disc)
+    oy, ohc, ohl = oracle_core(inp, w, disc)
+    assert_close(y, oy, "y")
+    assert_close(hl, ohl, "h_last")
+    if w.hcache:
+        assert_close(hc, ohc, "h_cache")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_h0_ungated_no_skip(disc):
+    w = gen.SMALL.with_(name="h0", batch=2, seq_len=2100, d_inner=96, h0=True)
+    inp = gen.generate(w, seed_offset=8)
+    for gated, dvec in ((False, True), (True, False), (False, False)):
+        y, _, hl = run_core(inp, w, disc, h0=inp["h0"], h_cache=False, gated=gated, dvec=dvec)
+        oy, _, ohl = oracle_core(inp, w, disc, h0=inp["h0"], h_cache=False, gated=gated,
+                                 dvec=dvec)
+        assert_close(y, oy, f"y gated={gated} dvec={dvec}")
+        assert_close(hl, ohl, "h_last")
+
+
+def test_zero_length_sequence_defines_h_last():
+    import torch
+    w = gen.SMALL.with_(batch=2, seq_len=4, d_inner=64, h0=True)
+    inp = gen.generate(w, seed_offset=9)
+    d = {k: dev(v) for k, v in inp.items()}
+    empty = torch.empty((0, 64), device="cuda")
+    empty_n = torch.empty((0, 16), device="cuda")
+    for h0 in (d["h0"], None):
+        hl = nan_like((2, 64, 16))
+        mss.mamba1_core(empty, d["w_conv"], None, empty, d["A_log"], empty_n, empty_n, None,
+                        None, h0, batch=2, seq_len=0, disc="zoh", h_last=hl, out=empty)
+        torch.cuda.synchronize()
+        want = inp["h0"] if h0 is not None else np.zeros((2, 64, 16))
+        assert np.array_equal(host(hl), want)
+
+
+# ---------------------------------------------------------------------------
+# invariants that hold bit-exactly on the GPU
+
+
+def test_deterministic_and_causal_and_clamp_invariant():
+    w = gen.SMALL.with_(name="inv", batch=2, seq_len=3000, d_inner=128, alog_clamp_frac=0.2)
+    inp = gen.generate(w, seed_offset=10)
+    y0, _, _ = run_core(inp, w, "zoh", h_cache=False)
+    y1, _, _ = run_core(inp, w, "zoh", h_cache=False)
+    assert np.array_equal(y0, y1), "two runs differ"
+    # causality: perturb x at (b=1, t0); nothing before t0 may change
+    t0 = 1700
+    x2 = inp["x"].copy()
+    x2[w.seq_len + t0] += 1.0
+    y2, _, _ = run_core({**inp, "x": x2}, w, "zoh", h_cache=False)
+    a = y0.reshape(2, w.seq_len, -1)
+    b = y2.reshape(2, w.seq_len, -1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1, :t0], b[1, :t0])
+    assert np.all(a[1, t0] != b[1, t0])
+    # A_log outside [-10, 5] only matters through the clamp
+    al = inp["A_log"].copy()
+    al = np.where(al < -10, -30.0, np.where(al > 5, 40.0, al)).astype(np.float32)
+    y3, _, _ = run_core({**inp, "A_log": al}, w, "zoh", h_cache=False)
+    assert np.array_equal(y0, y3), "clamp invariance"
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_hcache_consistent_with_output(disc):
+    w = gen.SMALL
+    inp = gen.generate(w, seed_offset=11)
+    y, hc, _ = run_core(inp, w, disc)
+    u = oracle.conv1d_silu(inp["x"], inp["w_conv"], inp["b_conv"], batch=w.batch,
+                           seq_len=w.seq_len)
+    C = inp["C"].astype(np.float64).reshape(w.batch, w.seq_len, w.d_state)
+    yy = np.einsum("bldn,bln->bld", hc, C).reshape(w.M, w.d_inner) + inp["D_vec"] * u
+    z = inp["z"].astype(np.float64)
+    assert_close(y, yy * z / (1 + np.exp(-z)), "y vs (sum C hCache + D u) SiLU(z)", tol=2e-4)
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_steps_match_sequence(disc):
+    """64 decode steps from a zero state equal the sequence kernel over L = 64."""
+    import torch
+    w = gen.SMALL.with_(name="steps", batch=4, seq_len=64, d_inner=200, b_conv="normal")
+    inp = gen.generate(w, seed_offset=12)
+    y_seq, hc, _ = run_core(inp, w, disc, h_cache=True)
+    B, L, D, N, K = w.batch, w.seq_len, w.d_inner, w.d_state, w.d_conv
+    d = {k: dev(v) for k, v in inp.items()}
+    x = d["x"].view(B, L, D)
+    z = d["z"].view(B, L, D)
+    dl = d["delta"].view(B, L, D)
+    Bm = d["B"].view(B, L, N)
+    Cm = d["C"].view(B, L, N)
+    h = torch.zeros((B, D, N), device="cuda")
+    cs = torch.zeros((B, K - 1, D), device="cuda")
+    ys = []
+    for t in range(L):
+        y = mss.selective_step(x[:, t].contiguous(), z[:, t].contiguous(), dl[:, t].contiguous(),
+                               d["A_log"], Bm[:, t].contiguous(), Cm[:, t].contiguous(),
+                               d["D_vec"], d["w_conv"], d["b_conv"], cs, h, disc=disc)
+        ys.append(host(y))
+        assert_close(host(h), hc[:, t], f"h at t={t}")
+    assert_close(np.stack(ys, 1).reshape(B * L, D), y_seq, "y")
