@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, AMD published
 METRIC = "selective-scan M·D elements/s and achieved HBM GB/s (% of peak), 1 MI355X"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mamba1_core_b4_l8192_d5120.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mamba1_core_b4_l8192_d5120.txt")
+COPY_BYTES = 1 << 30                      # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = ("scan_kernel.hip", "device_math.h", "launch.h")
 
 
@@ -44,16 +45,31 @@ def algorithmic_bytes(w) -> int:
 
 
 def measured_traffic(digest: str):
-    """HBM bytes per launch from rocprofv3 counters, if they were taken on this
-    exact kernel source; else None."""
+    """HBM bytes per launch of the fused kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counters (calibrated on a plain copy), read from the committed
+    summary, if it was taken on this exact kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith(" "))
+    except OSError:
         return None
-    if t.get("kernel_digest") != digest:
+    if kv.get("kernel_digest", "").strip() != digest:
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return float(kv["hbm_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(reps: int):
+    """A plain device copy of COPY_BYTES, for calibrating HBM byte counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, inp, disc, target_s=15.0):
@@ -90,11 +106,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--disc", default="zoh", choices=("zoh", "euler"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
 
     import torch
     import mamba_selective_scan_causal_amd as mss
