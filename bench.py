@@ -72,6 +72,67 @@ def copy_calibration(reps: int):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
+def _time_ms(fn, stream, reps, warm=2):
+    """Mean hipEvent time of fn() on `stream`, in ms."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extras(w, d, y, disc, stream):
+    """Side measurements: the other discretisation, the unfused path (conv
+    kernel, then the scan on u), and the decode workload (256 sequences x
+    5120 channels, 64 consecutive single-token steps)."""
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+    res = {}
+    other = "euler" if disc == "zoh" else "zoh"
+    kw = dict(batch=w.batch, seq_len=w.seq_len, out=y, stream=stream)
+    t = _time_ms(lambda: mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"],
+                                         d["B"], d["C"], d["D_vec"], d["z"], None, disc=other,
+                                         **kw), stream, 10)
+    res[f"fused_{other}_ms"] = t
+    u = torch.empty_like(d["x"])
+    tc = _time_ms(lambda: mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch,
+                                          seq_len=w.seq_len, out=u, stream=stream), stream, 10)
+    ts = _time_ms(lambda: mss.selective_scan(u, d["delta"], d["A_log"], d["B"], d["C"],
+                                             d["D_vec"], d["z"], None, disc=disc, **kw),
+                  stream, 10)
+    MD = w.M * w.d_inner
+    res["unfused"] = {"conv1d_silu_ms": tc, "conv1d_silu_GBps": 8 * MD / tc / 1e6,
+                      "scan_on_u_ms": ts, "total_ms": tc + ts}
+    del u
+    dw = gen.DECODE
+    dinp = gen.generate(dw)
+    dd = {k: torch.from_numpy(v).cuda() for k, v in dinp.items()}
+    yd = torch.empty((dw.batch, dw.d_inner), device="cuda")
+
+    def decode64():
+        for s_ in range(dw.seq_len):
+            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
+                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
+                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd,
+                               stream=stream)
+
+    t64 = _time_ms(decode64, stream, 3, warm=1)
+    BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
+    step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
+    res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
+                     "algorithmic_bytes_per_step": step_bytes,
+                     "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
+                     "note": "h + conv window (~100 MB) fit the 256 MB last-level cache"}
+    return res
+
+
 def cpu_baseline(w, inp, disc, target_s=15.0):
     """The oracle as it stands, on a bounded sample of whole (b, d) columns of
     the same workload, on all host cores it may use."""
@@ -106,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--disc", default="zoh", choices=("zoh", "euler"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the side measurements (other mode, unfused path, decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -175,6 +238,8 @@ def main():
                      "kernel_ms": kern_ms, "algorithmic_bytes": abytes,
                      "kernel_digest": digest},
     }
+    if not args.no_extras:
+        out["extra"] = extras(w, d, y, args.disc, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.disc)
     print(json.dumps(out), flush=True)

@@ -179,19 +179,52 @@ EDGE = [
     ("bias", dict(batch=2, seq_len=500, d_inner=128, b_conv="normal")),
     ("slow_decay_full_replay", dict(batch=2, seq_len=3000, d_inner=64, alog_clamp_frac=1.0)),
     ("tiny_steps", dict(batch=2, seq_len=1500, d_inner=64, delta_mean=-9.0, delta_var=1.0)),
+    # hCache written by waves whose segment starts after a replay
+    ("hcache_segments", dict(batch=1, seq_len=2048, d_inner=64, hcache=True)),
+    ("hcache_segments_ragged", dict(batch=2, seq_len=1300, d_inner=100, hcache=True)),
 ]
+
+
+def _mixed_regimes(inp, w):
+    """delta alternates every 96 steps between N(-2, 0.5) and N(-9, 1), so one
+    sequence mixes fast blocks, slow (nearly integrating) blocks and long
+    replays; A_log spread over [-4, 4] like a trained model's."""
+    g = np.random.default_rng(77)
+    t = np.arange(w.seq_len)
+    slow = ((t // 96) % 2 == 1)[None, :, None]
+    d = inp["delta"].reshape(w.batch, w.seq_len, w.d_inner)
+    d = np.where(slow, g.normal(-9.0, 1.0, d.shape), g.normal(-2.0, 0.7, d.shape))
+    inp = dict(inp)
+    inp["delta"] = d.reshape(w.M, w.d_inner).astype(np.float32)
+    inp["A_log"] = g.uniform(-4.0, 4.0, inp["A_log"].shape).astype(np.float32)
+    return inp
 
 
 @pytest.mark.parametrize("disc", DISCS)
 @pytest.mark.parametrize("name,over", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_cases(name, over, disc):
-    w = gen.SMALL.with_(name=name, hcache=over.get("seq_len", 0) <= 1000, **over)
+    over = dict(over)
+    hcache = over.pop("hcache", over.get("seq_len", 0) <= 1000)
+    w = gen.SMALL.with_(name=name, hcache=hcache, **over)
     inp = gen.generate(w, seed_offset=7)
     y, hc, hl = run_core(inp, w, disc)
     oy, ohc, ohl = oracle_core(inp, w, disc)
     assert_close(y, oy, "y")
     assert_close(hl, ohl, "h_last")
     if w.hcache:
+        assert_close(hc, ohc, "h_cache")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("hcache", (False, True))
+def test_mixed_fast_and_slow_blocks(disc, hcache):
+    w = gen.SMALL.with_(name="mixed", batch=2, seq_len=2900, d_inner=128, hcache=hcache)
+    inp = _mixed_regimes(gen.generate(w, seed_offset=13), w)
+    y, hc, hl = run_core(inp, w, disc)
+    oy, ohc, ohl = oracle_core(inp, w, disc)
+    assert_close(y, oy, "y")
+    assert_close(hl, ohl, "h_last")
+    if hcache:
         assert_close(hc, ohc, "h_cache")
 
 
