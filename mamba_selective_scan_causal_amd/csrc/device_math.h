@@ -51,6 +51,13 @@ __device__ __forceinline__ float a_cont(float a_log) {
 typedef const __attribute__((address_space(4))) float cfloat;
 __device__ __forceinline__ const cfloat* as_const(const float* p) { return (const cfloat*)p; }
 
+// The same A from the hardware exponential (relative error ~|c| 6e-8 + 1 ulp,
+// at most ~4e-7), for kernels that rebuild A on every call.
+__device__ __forceinline__ float a_cont_fast(float a_log) {
+    const float c = __builtin_fminf(__builtin_fmaxf(a_log, -10.0f), 5.0f);
+    return -ex2(c * kLog2e);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
 

@@ -18,95 +18,164 @@ namespace {
 
 constexpr float kSmallX = 0.015625f;          // same ZOH expm1 switch as the scan
 
+// Batch rows per wave: the per-channel parameters (A, 1/A, conv taps) are
+// loaded and transformed once for kRows rows, and all loads of the rows are
+// issued before any arithmetic so that their latencies overlap.
+constexpr int kRows = 2;
+
 template <int DISC, int KS, int NS>
 __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
     constexpr int NR = NS > 0 ? NS : kMaxN;
     constexpr int KR = KS > 0 ? KS : kMaxK;
+    constexpr bool kStageBC = NS == 16 && kRows * 32 == kWave;
+    __shared__ __align__(16) float bcs[kWave];
     const int N = NS > 0 ? NS : a.N;
     const int K = KS > 0 ? KS : a.K;
     const int64_t tiles = (a.D + kWave - 1) / kWave;
-    const int64_t nblk = a.B * tiles;
+    const int64_t groups = (a.B + kRows - 1) / kRows;
+    const int64_t nblk = groups * tiles;
     for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t b = blk / tiles;
-        const int64_t d_raw = (blk - b * tiles) * kWave + threadIdx.x;
+        const int64_t g = blk / tiles;
+        const int64_t d_raw = (blk - g * tiles) * kWave + threadIdx.x;
         const bool valid = d_raw < a.D;
         const int64_t d = valid ? d_raw : a.D - 1;
-        const int64_t bd = b * a.D + d;
+        int64_t bs[kRows];
+        bool live[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; r++) {
+            const int64_t b = g * kRows + r;
+            live[r] = b < a.B;            // wave-uniform
+            bs[r] = live[r] ? b : a.B - 1;
+        }
 
-        // conv over (window, x).  Registers hold the window newest first:
-        // prev[k-1] = input k steps back = conv_state[K-1-k] (oldest-first
-        // buffer), so every register index is a compile-time constant.
-        const float xv = a.x[bd];
-        float prev[KR > 1 ? KR - 1 : 1];
+        // --- every load first: B/C rows, per-row inputs and state, then the
+        // per-channel parameters.  With N = 16 the B and C rows of the
+        // wave's kRows batch entries are exactly one float per lane: loaded
+        // as one vector load together with the rest, staged through LDS and
+        // read back as broadcasts.
+        float bc = 0.0f;
+        if constexpr (kStageBC) {
+            const uint32_t l = threadIdx.x, r = l / 32, j = l % 32;
+            bc = j < 16 ? a.B_in[bs[r] * 16 + j] : a.C_in[bs[r] * 16 + (j - 16)];
+        }
+        float xv[kRows], dl[kRows], zv[kRows], h[kRows][NR];
+        float prev[kRows][KR > 1 ? KR - 1 : 1];   // prev[r][k-1]: input k steps back
 #pragma unroll
-        for (int k = 1; k < KR; k++)
-            prev[k - 1] = k < K ? a.conv_state[(b * (K - 1) + (K - 1 - k)) * a.D + d] : 0.0f;
-        float acc = a.b_conv ? a.b_conv[d] : 0.0f;
-        acc = __builtin_fmaf(a.w_conv[d * K], xv, acc);
+        for (int r = 0; r < kRows; r++) {
+            const int64_t bd = bs[r] * a.D + d;
+            xv[r] = a.x[bd];
+            dl[r] = a.delta[bd];
+            zv[r] = a.z ? a.z[bd] : 0.0f;
 #pragma unroll
-        for (int k = 1; k < KR; k++)
-            if (k < K) acc = __builtin_fmaf(a.w_conv[d * K + k], prev[k - 1], acc);
-        const float u = silu(acc);
-        const float dv = softplus(a.delta[bd]);
+            for (int k = 1; k < KR; k++)
+                prev[r][k - 1] =
+                    k < K ? a.conv_state[(bs[r] * (K - 1) + (K - 1 - k)) * a.D + d] : 0.0f;
+            const float* hp = a.h + bd * N;
+            if constexpr (NS > 0 && NS % 4 == 0) {
+#pragma unroll
+                for (int n = 0; n < NR; n += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(hp + n);
+                    h[r][n] = v.x; h[r][n + 1] = v.y; h[r][n + 2] = v.z; h[r][n + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < NR; n++) h[r][n] = n < N ? hp[n] : 0.0f;
+            }
+        }
+        float A2[NR], Ai[NR], w[KR];
+#pragma unroll
+        for (int n = 0; n < NR; n++) {
+            const float A = (NS > 0 || n < N) ? a_cont_fast(a.A_log[d * N + n]) : -1.0f;
+            A2[n] = A * kLog2e;
+            Ai[n] = rcp(A);
+        }
+#pragma unroll
+        for (int k = 0; k < KR; k++) w[k] = k < K ? a.w_conv[d * K + k] : 0.0f;
+        const float bias = a.b_conv ? a.b_conv[d] : 0.0f;
+        const float dvec = a.D_vec ? a.D_vec[d] : 0.0f;
 
-        float h[NR], A2[NR], Ai[NR];
-        float* __restrict__ hp = a.h + bd * N;
-        if constexpr (NS > 0 && NS % 4 == 0) {
+        float Bv[kRows][NR], Cv[kRows][NR];
+        if constexpr (kStageBC) {
+            bcs[threadIdx.x] = bc;       // one wave per workgroup: program order suffices
+            const float4* q = reinterpret_cast<const float4*>(bcs);
 #pragma unroll
-            for (int n = 0; n < NR; n += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(hp + n);
-                h[n] = v.x; h[n + 1] = v.y; h[n + 2] = v.z; h[n + 3] = v.w;
+            for (int r = 0; r < kRows; r++) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float4 bq = q[r * 8 + i], cq = q[r * 8 + 4 + i];
+                    Bv[r][4 * i] = bq.x; Bv[r][4 * i + 1] = bq.y;
+                    Bv[r][4 * i + 2] = bq.z; Bv[r][4 * i + 3] = bq.w;
+                    Cv[r][4 * i] = cq.x; Cv[r][4 * i + 1] = cq.y;
+                    Cv[r][4 * i + 2] = cq.z; Cv[r][4 * i + 3] = cq.w;
+                }
             }
         } else {
 #pragma unroll
-            for (int n = 0; n < NR; n++) h[n] = n < N ? hp[n] : 0.0f;
-        }
+            for (int r = 0; r < kRows; r++) {
+                const cfloat* Br = as_const(a.B_in + bs[r] * N);
+                const cfloat* Cr = as_const(a.C_in + bs[r] * N);
 #pragma unroll
-        for (int n = 0; n < NR; n++) {
-            const float A = (NS > 0 || n < N) ? a_cont(a.A_log[d * N + n]) : -1.0f;
-            A2[n] = A * kLog2e;
-            Ai[n] = 1.0f / A;
-        }
-        const cfloat* Br = as_const(a.B_in + b * N);
-        const cfloat* Cr = as_const(a.C_in + b * N);
-        float yv = (a.D_vec ? a.D_vec[d] : 0.0f) * u;
-        // The decay is applied as h + m h with m = expm1(dv A) (a cubic when
-        // |dv A| < 2^-6): a nearly-integrating state keeps its accuracy over
-        // any number of steps.  Memory-bound, so no fast path is needed.
-        const float dvu = dv * u;
-#pragma unroll
-        for (int n = 0; n < NR; n++) {
-            if (NS > 0 || n < N) {
-                const float x2 = dv * A2[n];
-                const float ab = ex2(x2);
-                const float x = x2 * kLn2;
-                const float p = x * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 6.0f, 0.5f), 1.0f);
-                const float m = __builtin_fabsf(x) < kSmallX ? p : ab - 1.0f;
-                if constexpr (DISC == MSS_DISC_EULER) {
-                    h[n] = __builtin_fmaf(dvu, Br[n], __builtin_fmaf(m, h[n], h[n]));
-                } else {
-                    const float kk = (u * Ai[n]) * Br[n];
-                    h[n] = __builtin_fmaf(m, h[n] + kk, h[n]);
+                for (int n = 0; n < NR; n++) {
+                    Bv[r][n] = n < N ? Br[n] : 0.0f;
+                    Cv[r][n] = n < N ? Cr[n] : 0.0f;
                 }
-                yv = __builtin_fmaf(Cr[n], h[n], yv);
             }
         }
-        if (valid) {
-            a.y[bd] = a.z ? yv * silu(a.z[bd]) : yv;
-            if constexpr (NS > 0 && NS % 4 == 0) {
+
 #pragma unroll
-                for (int n = 0; n < NR; n += 4)
-                    *reinterpret_cast<float4*>(hp + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
-            } else {
-#pragma unroll
-                for (int n = 0; n < NR; n++)
-                    if (n < N) hp[n] = h[n];
-            }
-            // shifted window: position K-1-k now holds the input k-1 steps back
+        for (int r = 0; r < kRows; r++) {
+            if (!live[r]) continue;
+            // conv over (window, x): tap 0 is the new input
+            float acc = __builtin_fmaf(w[0], xv[r], bias);
 #pragma unroll
             for (int k = 1; k < KR; k++)
-                if (k < K)
-                    a.conv_state[(b * (K - 1) + (K - 1 - k)) * a.D + d] = k == 1 ? xv : prev[k >= 2 ? k - 2 : 0];
+                if (k < K) acc = __builtin_fmaf(w[k], prev[r][k - 1], acc);
+            const float u = silu(acc);
+            const float dv = softplus(dl[r]);
+            float yv = dvec * u;
+            // The decay is applied as h + m h with m = expm1(dv A) (a cubic when
+            // |dv A| < 2^-6): a nearly-integrating state keeps its accuracy over
+            // any number of steps.  Memory-bound, so no fast path is needed.
+            const float dvu = dv * u;
+#pragma unroll
+            for (int n = 0; n < NR; n++) {
+                if (NS > 0 || n < N) {
+                    const float x2 = dv * A2[n];
+                    const float ab = ex2(x2);
+                    const float x = x2 * kLn2;
+                    const float p =
+                        x * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 6.0f, 0.5f), 1.0f);
+                    const float m = __builtin_fabsf(x) < kSmallX ? p : ab - 1.0f;
+                    if constexpr (DISC == MSS_DISC_EULER) {
+                        h[r][n] = __builtin_fmaf(dvu, Bv[r][n], __builtin_fmaf(m, h[r][n], h[r][n]));
+                    } else {
+                        const float kk = (u * Ai[n]) * Bv[r][n];
+                        h[r][n] = __builtin_fmaf(m, h[r][n] + kk, h[r][n]);
+                    }
+                    yv = __builtin_fmaf(Cv[r][n], h[r][n], yv);
+                }
+            }
+            if (valid) {
+                const int64_t bd = bs[r] * a.D + d;
+                a.y[bd] = a.z ? yv * silu(zv[r]) : yv;
+                float* hp = a.h + bd * N;
+                if constexpr (NS > 0 && NS % 4 == 0) {
+#pragma unroll
+                    for (int n = 0; n < NR; n += 4)
+                        *reinterpret_cast<float4*>(hp + n) =
+                            make_float4(h[r][n], h[r][n + 1], h[r][n + 2], h[r][n + 3]);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NR; n++)
+                        if (n < N) hp[n] = h[r][n];
+                }
+                // shifted window: position K-1-k now holds the input k-1 steps back
+#pragma unroll
+                for (int k = 1; k < KR; k++)
+                    if (k < K)
+                        a.conv_state[(bs[r] * (K - 1) + (K - 1 - k)) * a.D + d] =
+                            k == 1 ? xv[r] : prev[r][k >= 2 ? k - 2 : 0];
+            }
         }
     }
 }
@@ -128,7 +197,7 @@ hipError_t launch_k(const StepArgs& a, unsigned grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_step(const StepArgs& a, hipStream_t st) {
-    const int64_t nblk = a.B * ((a.D + kWave - 1) / kWave);
+    const int64_t nblk = ((a.B + kRows - 1) / kRows) * ((a.D + kWave - 1) / kWave);
     const unsigned grid = static_cast<unsigned>(nblk < (1 << 30) ? nblk : (1 << 30));
     return a.disc == MSS_DISC_EULER ? launch_k<MSS_DISC_EULER>(a, grid, st)
                                     : launch_k<MSS_DISC_ZOH>(a, grid, st);
