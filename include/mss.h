@@ -21,7 +21,8 @@
  *     on the current HIP device, allocated and owned by the caller.  The
  *     library allocates nothing, keeps no device state and never frees a
  *     caller buffer.
- *   - Every pointer must be 16-byte aligned (MSS_EALIGN otherwise).
+ *   - Every pointer must be 16-byte aligned (MSS_EALIGN otherwise), except
+ *     the activation and B/C tensors of the *_strided entry points (4 bytes).
  *   - Outputs may not overlap any input (MSS_EALIAS), except the state
  *     buffers of mss_selective_step, which are updated in place by design.
  *   - Work is enqueued on `stream` (NULL = the null stream) and the call
@@ -110,6 +111,44 @@ int mss_mamba1_core(const mss_dims* dims, int disc, const float* x, const float*
                     const float* B, const float* C, const float* D_vec, const float* z,
                     const float* h0, float* y, float* h_cache, float* h_last,
                     hipStream_t stream);
+
+/* Row strides (in elements) of the activation-shaped tensors, for reading
+ * them in place as column slices of wider buffers: x and z as the two halves
+ * of the (M, 2D) input-projection output, delta / B / C as column ranges of
+ * the (M, R+2N) x-projection output.  The pages split these with a strided
+ * column gather (COL_SLICE_WGSL / dispatchColumnSlice, which replaced a
+ * prefix copy that was wrong for more than one row; builderforce-memory-engine
+ * 2026.7.14 -> 2026.9.28, src/model/mamba1_block.ts); the strided entry
+ * points make that gather unnecessary.
+ * Row r of tensor T starts at T + r * T_stride.  Each stride must be at least
+ * the row width (D for x, z, delta, y; N for B, C).  In the strided entry
+ * points x (or u), z, delta, B, C and y need only 4-byte alignment; the
+ * remaining tensors keep the 16-byte rule. */
+typedef struct mss_strides {
+    int32_t struct_size;    /* sizeof(mss_strides) */
+    int32_t reserved;       /* must be 0 */
+    int64_t x;              /* x (core) or u (scan) */
+    int64_t z;
+    int64_t delta;
+    int64_t B;
+    int64_t C;
+    int64_t y;
+} mss_strides;
+
+/* mss_selective_scan with row strides; same semantics otherwise. */
+int mss_selective_scan_strided(const mss_dims* dims, const mss_strides* strides, int disc,
+                               const float* u, const float* delta, const float* A_log,
+                               const float* B, const float* C, const float* D_vec,
+                               const float* z, const float* h0, float* y, float* h_cache,
+                               float* h_last, hipStream_t stream);
+
+/* mss_mamba1_core with row strides; same semantics otherwise. */
+int mss_mamba1_core_strided(const mss_dims* dims, const mss_strides* strides, int disc,
+                            const float* x, const float* w_conv, const float* b_conv,
+                            const float* delta, const float* A_log, const float* B,
+                            const float* C, const float* D_vec, const float* z,
+                            const float* h0, float* y, float* h_cache, float* h_last,
+                            hipStream_t stream);
 
 /* One single-token recurrent step (decode) with carried state; the plainest
  * reading of steps 4-9 for L = 1 with the conv window and h carried over.

@@ -48,7 +48,18 @@ def make_dims(batch, seq_len, d_inner, d_state, d_conv=1) -> Dims:
     return Dims(ctypes.sizeof(Dims), 0, batch, seq_len, d_inner, d_state, d_conv)
 
 
+class Strides(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x", ctypes.c_int64), ("z", ctypes.c_int64), ("delta", ctypes.c_int64),
+                ("B", ctypes.c_int64), ("C", ctypes.c_int64), ("y", ctypes.c_int64)]
+
+
+def make_strides(x, z, delta, B, C, y) -> Strides:
+    return Strides(ctypes.sizeof(Strides), 0, x, z, delta, B, C, y)
+
+
 EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_selective_step",
+           "mss_selective_scan_strided", "mss_mamba1_core_strided",
            "mss_strerror", "mss_version", "mss_last_hip_error")
 
 _lib = None
@@ -68,8 +79,12 @@ def lib():
         L.mss_selective_scan.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p]
         L.mss_mamba1_core.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p, p, p]
         L.mss_selective_step.argtypes = [dp, i, p, p, p, p, p, p, p, p, p, p, p, p, p]
+        sp = ctypes.POINTER(Strides)
+        L.mss_selective_scan_strided.argtypes = [dp, sp, i] + [p] * 12
+        L.mss_mamba1_core_strided.argtypes = [dp, sp, i] + [p] * 14
         for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
-                  "mss_selective_step", "mss_version", "mss_last_hip_error"):
+                  "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
+                  "mss_version", "mss_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         L.mss_strerror.argtypes = [ctypes.c_int]
         L.mss_strerror.restype = ctypes.c_char_p
@@ -114,6 +129,28 @@ def _ptr(t, name, shape, required=True):
     return t.data_ptr() or None
 
 
+def _rows(t, name, rows, cols, required=True):
+    """(pointer, row stride) of a (rows, cols) fp32 GPU tensor whose rows may be
+    strided (a column slice of a wider buffer); columns must be unit-stride."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None, cols
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 GPU tensor")
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name}: expected shape {(rows, cols)}, got {tuple(t.shape)}")
+    if rows > 0 and cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: columns must be contiguous")
+    ld = t.stride(0) if rows > 1 else cols
+    return (t.data_ptr() or None), ld
+
+
+def _dense(*ts):
+    return all(t is None or t.is_contiguous() for t in ts)
+
+
 def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -150,16 +187,32 @@ def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
                    h_cache=False, h_last=False, out=None, stream=None):
     """Selective scan + gate on a given u.  Returns (y, h_cache, h_last).
 
-    ``h_cache`` / ``h_last``: False (skip), True (allocate) or an output tensor."""
+    ``h_cache`` / ``h_last``: False (skip), True (allocate) or an output tensor.
+    u, delta, z, B, C and ``out`` may be row-strided views (column slices)."""
     D, N = A_log.shape
     M = batch * seq_len
     y, hc, hl = _scan_outputs(u, batch, seq_len, D, N, out, h_cache, h_last)
     dims = make_dims(batch, seq_len, D, N, 1)
-    _check("mss_selective_scan", lib().mss_selective_scan(
-        ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
-        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
-        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
-        _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
+    common = (_ptr(A_log, "A_log", (D, N)),)
+    tail = (_ptr(D_vec, "D_vec", (D,), False),)
+    if _dense(u, delta, B, C, z, y):
+        _check("mss_selective_scan", lib().mss_selective_scan(
+            ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
+            *common, _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)), *tail,
+            _ptr(z, "z", (M, D), False), _ptr(h0, "h0", (batch, D, N), False),
+            _ptr(y, "y", (M, D)), _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+            _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
+        return y, hc, hl
+    pu, lu = _rows(u, "u", M, D)
+    pd, ldd = _rows(delta, "delta", M, D)
+    pb, lb = _rows(B, "B", M, N)
+    pc, lc = _rows(C, "C", M, N)
+    pz, lz = _rows(z, "z", M, D, False)
+    py, ly = _rows(y, "y", M, D)
+    st = make_strides(lu, lz, ldd, lb, lc, ly)
+    _check("mss_selective_scan_strided", lib().mss_selective_scan_strided(
+        ctypes.byref(dims), ctypes.byref(st), _disc(disc), pu, pd, *common, pb, pc, *tail, pz,
+        _ptr(h0, "h0", (batch, D, N), False), py,
         _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
         _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
     return y, hc, hl
@@ -167,18 +220,35 @@ def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
 
 def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
                 seq_len, disc, h_cache=False, h_last=False, out=None, stream=None):
-    """Fused conv1d + SiLU + selective scan + gate from x.  Returns (y, h_cache, h_last)."""
+    """Fused conv1d + SiLU + selective scan + gate from x.  Returns (y, h_cache, h_last).
+
+    x, delta, z, B, C and ``out`` may be row-strided views (column slices)."""
     D, N = A_log.shape
     K = w_conv.shape[1]
     M = batch * seq_len
     y, hc, hl = _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last)
     dims = make_dims(batch, seq_len, D, N, K)
-    _check("mss_mamba1_core", lib().mss_mamba1_core(
-        ctypes.byref(dims), _disc(disc), _ptr(x, "x", (M, D)), _ptr(w_conv, "w_conv", (D, K)),
-        _ptr(b_conv, "b_conv", (D,), False), _ptr(delta, "delta", (M, D)),
-        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
-        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
-        _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
+    conv = (_ptr(w_conv, "w_conv", (D, K)), _ptr(b_conv, "b_conv", (D,), False))
+    if _dense(x, delta, B, C, z, y):
+        _check("mss_mamba1_core", lib().mss_mamba1_core(
+            ctypes.byref(dims), _disc(disc), _ptr(x, "x", (M, D)), *conv,
+            _ptr(delta, "delta", (M, D)), _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)),
+            _ptr(C, "C", (M, N)), _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
+            _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
+            _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+            _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
+        return y, hc, hl
+    px, lx = _rows(x, "x", M, D)
+    pd, ldd = _rows(delta, "delta", M, D)
+    pb, lb = _rows(B, "B", M, N)
+    pc, lc = _rows(C, "C", M, N)
+    pz, lz = _rows(z, "z", M, D, False)
+    py, ly = _rows(y, "y", M, D)
+    st = make_strides(lx, lz, ldd, lb, lc, ly)
+    _check("mss_mamba1_core_strided", lib().mss_mamba1_core_strided(
+        ctypes.byref(dims), ctypes.byref(st), _disc(disc), px, *conv, pd,
+        _ptr(A_log, "A_log", (D, N)), pb, pc, _ptr(D_vec, "D_vec", (D,), False), pz,
+        _ptr(h0, "h0", (batch, D, N), False), py,
         _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
         _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
     return y, hc, hl

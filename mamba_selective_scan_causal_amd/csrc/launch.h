@@ -18,6 +18,10 @@ struct ScanShape {
     int64_t tiles_per_b;
     int64_t total;
     int64_t seg;
+    // row strides in elements (D, D, D, N, N, D when dense)
+    int64_t ld_src, ld_z, ld_delta, ld_B, ld_C, ld_y;
+    bool bc_vec;              // B and C rows 16-byte aligned: staged block loads
+    bool dense;               // strides are exactly D (activations) and N (B, C)
 };
 
 struct ScanArgs {

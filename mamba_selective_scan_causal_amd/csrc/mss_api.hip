@@ -60,22 +60,39 @@ struct Checker {
     int status = MSS_OK;
     std::vector<Span> ins, outs;
 
-    // A tensor of `elems` fp32 values.  Required tensors may be NULL only when
-    // they hold no elements.
-    void in(const float* p, int64_t elems, bool required) { add(ins, p, elems, required); }
-    void out(float* p, int64_t elems, bool required) { add(outs, p, elems, required); }
+    // A dense tensor of `elems` fp32 values (16-byte aligned).  Required
+    // tensors may be NULL only when they hold no elements.
+    void in(const float* p, int64_t elems, bool required) { add(ins, p, elems * 4, required, 16); }
+    void out(float* p, int64_t elems, bool required) { add(outs, p, elems * 4, required, 16); }
+    // `rows` rows of `width` fp32 values, row r at p + r * stride (4-byte aligned).
+    void in_rows(const float* p, int64_t rows, int64_t width, int64_t stride, bool required) {
+        add(ins, p, rows_bytes(rows, width, stride), required, 4);
+    }
+    void out_rows(float* p, int64_t rows, int64_t width, int64_t stride, bool required) {
+        add(outs, p, rows_bytes(rows, width, stride), required, 4);
+    }
 
-    void add(std::vector<Span>& v, const void* p, int64_t elems, bool required) {
+    int64_t rows_bytes(int64_t rows, int64_t width, int64_t stride) {
+        if (rows <= 0 || width <= 0) return 0;
+        int64_t span;
+        if (stride < width || !count(span, {rows - 1, stride}) || span > INT64_MAX / 8 - width) {
+            if (status == MSS_OK) status = MSS_EINVAL;
+            return 0;
+        }
+        return (span + width) * 4;
+    }
+
+    void add(std::vector<Span>& v, const void* p, int64_t bytes, bool required, uintptr_t align) {
         if (status != MSS_OK) return;
         if (!p) {
-            if (required && elems > 0) status = MSS_EINVAL;
+            if (required && bytes > 0) status = MSS_EINVAL;
             return;
         }
-        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) {
+        if (reinterpret_cast<uintptr_t>(p) % align != 0) {
             status = MSS_EALIGN;
             return;
         }
-        v.push_back({p, elems * 4});
+        v.push_back({p, bytes});
     }
 
     int finish() {
@@ -123,7 +140,8 @@ int cu_count() {
     return c;
 }
 
-mss::ScanShape scan_shape(const mss_dims* dims) {
+mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const float* B,
+                          const float* C) {
     static const int64_t waves_per_cu = env_or("MSS_SCAN_WAVES_PER_CU", 8);
     static const int64_t min_seg = env_or("MSS_SCAN_MIN_SEG", 512);
     mss::ScanShape s;
@@ -138,37 +156,73 @@ mss::ScanShape scan_shape(const mss_dims* dims) {
     int64_t seg = (s.total + target - 1) / target;
     if (seg < min_seg) seg = min_seg;
     s.seg = seg;
+    s.ld_src = ld.x;
+    s.ld_z = ld.z;
+    s.ld_delta = ld.delta;
+    s.ld_B = ld.B;
+    s.ld_C = ld.C;
+    s.ld_y = ld.y;
+    s.bc_vec = reinterpret_cast<uintptr_t>(B) % 16 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+               ld.B % 4 == 0 && ld.C % 4 == 0;
+    s.dense = ld.x == s.D && ld.z == s.D && ld.delta == s.D && ld.y == s.D && ld.B == s.N &&
+              ld.C == s.N;
     return s;
 }
 
-int scan_common(const mss_dims* dims, int disc, bool fused, const float* src, const float* w_conv,
-                const float* b_conv, const float* delta, const float* A_log, const float* B,
-                const float* C, const float* D_vec, const float* z, const float* h0, float* y,
-                float* h_cache, float* h_last, hipStream_t stream) {
+mss_strides dense_strides(const mss_dims* dims) {
+    mss_strides s;
+    s.struct_size = sizeof(mss_strides);
+    s.reserved = 0;
+    s.x = s.z = s.delta = s.y = dims->d_inner;
+    s.B = s.C = dims->d_state;
+    return s;
+}
+
+// strided: the caller's strides (activations and B/C may be 4-byte aligned
+// column slices); otherwise dense tensors with the 16-byte rule everywhere.
+int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, int disc,
+                bool fused, const float* src, const float* w_conv, const float* b_conv,
+                const float* delta, const float* A_log, const float* B, const float* C,
+                const float* D_vec, const float* z, const float* h0, float* y, float* h_cache,
+                float* h_last, hipStream_t stream) {
     int st = check_dims(dims, true, fused);
     if (st != MSS_OK) return st;
     if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
+    if (strided && (!strides || strides->struct_size != static_cast<int32_t>(sizeof(mss_strides)) ||
+                    strides->reserved != 0))
+        return MSS_EINVAL;
+    const mss_strides ld = strided ? *strides : dense_strides(dims);
     const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
     const int64_t K = dims->d_conv;
-    int64_t MD, MN, DN, BDN, BLDN;
-    if (!count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) || !count(DN, {D, N}) ||
-        !count(BDN, {Bt, D, N}) || (h_cache && !count(BLDN, {Bt, L, D, N})))
+    int64_t M, MD, MN, DN, BDN, BLDN;
+    if (!count(M, {Bt, L}) || !count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) ||
+        !count(DN, {D, N}) || !count(BDN, {Bt, D, N}) ||
+        (h_cache && !count(BLDN, {Bt, L, D, N})))
         return MSS_EINVAL;
     if (!h_cache) BLDN = 0;
     Checker ck;
-    ck.in(src, MD, true);
+    if (strided) {
+        ck.in_rows(src, M, D, ld.x, true);
+        ck.in_rows(delta, M, D, ld.delta, true);
+        ck.in_rows(B, M, N, ld.B, true);
+        ck.in_rows(C, M, N, ld.C, true);
+        ck.in_rows(z, M, D, ld.z, false);
+        ck.out_rows(y, M, D, ld.y, true);
+    } else {
+        ck.in(src, MD, true);
+        ck.in(delta, MD, true);
+        ck.in(B, MN, true);
+        ck.in(C, MN, true);
+        ck.in(z, MD, false);
+        ck.out(y, MD, true);
+    }
     if (fused) {
         ck.in(w_conv, D * K, true);
         ck.in(b_conv, D, false);
     }
-    ck.in(delta, MD, true);
     ck.in(A_log, DN, true);
-    ck.in(B, MN, true);
-    ck.in(C, MN, true);
     ck.in(D_vec, D, false);
-    ck.in(z, MD, false);
     ck.in(h0, BDN, false);
-    ck.out(y, MD, true);
     ck.out(h_cache, BLDN, false);
     ck.out(h_last, BDN, false);
     st = ck.finish();
@@ -181,7 +235,7 @@ int scan_common(const mss_dims* dims, int disc, bool fused, const float* src, co
     }
     const mss::ScanArgs a{disc, fused, src, delta, A_log, B, C, D_vec, z, h0, w_conv, b_conv,
                           y, h_cache, h_last};
-    const hipError_t e = mss::launch_scan(a, scan_shape(dims), stream);
+    const hipError_t e = mss::launch_scan(a, scan_shape(dims, ld, B, C), stream);
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
@@ -213,16 +267,35 @@ int mss_selective_scan(const mss_dims* dims, int disc, const float* u, const flo
                        const float* A_log, const float* B, const float* C, const float* D_vec,
                        const float* z, const float* h0, float* y, float* h_cache, float* h_last,
                        hipStream_t stream) {
-    return scan_common(dims, disc, false, u, nullptr, nullptr, delta, A_log, B, C, D_vec, z, h0,
-                       y, h_cache, h_last, stream);
+    return scan_common(dims, nullptr, false, disc, false, u, nullptr, nullptr, delta, A_log, B,
+                       C, D_vec, z, h0, y, h_cache, h_last, stream);
+}
+
+int mss_selective_scan_strided(const mss_dims* dims, const mss_strides* strides, int disc,
+                               const float* u, const float* delta, const float* A_log,
+                               const float* B, const float* C, const float* D_vec,
+                               const float* z, const float* h0, float* y, float* h_cache,
+                               float* h_last, hipStream_t stream) {
+    return scan_common(dims, strides, true, disc, false, u, nullptr, nullptr, delta, A_log, B,
+                       C, D_vec, z, h0, y, h_cache, h_last, stream);
 }
 
 int mss_mamba1_core(const mss_dims* dims, int disc, const float* x, const float* w_conv,
                     const float* b_conv, const float* delta, const float* A_log, const float* B,
                     const float* C, const float* D_vec, const float* z, const float* h0, float* y,
                     float* h_cache, float* h_last, hipStream_t stream) {
-    return scan_common(dims, disc, true, x, w_conv, b_conv, delta, A_log, B, C, D_vec, z, h0, y,
-                       h_cache, h_last, stream);
+    return scan_common(dims, nullptr, false, disc, true, x, w_conv, b_conv, delta, A_log, B, C,
+                       D_vec, z, h0, y, h_cache, h_last, stream);
+}
+
+int mss_mamba1_core_strided(const mss_dims* dims, const mss_strides* strides, int disc,
+                            const float* x, const float* w_conv, const float* b_conv,
+                            const float* delta, const float* A_log, const float* B,
+                            const float* C, const float* D_vec, const float* z,
+                            const float* h0, float* y, float* h_cache, float* h_last,
+                            hipStream_t stream) {
+    return scan_common(dims, strides, true, disc, true, x, w_conv, b_conv, delta, A_log, B, C,
+                       D_vec, z, h0, y, h_cache, h_last, stream);
 }
 
 int mss_selective_step(const mss_dims* dims, int disc, const float* x, const float* z,

@@ -77,7 +77,9 @@ constexpr int kWarm = 0;     // state only
 constexpr int kOut = 1;      // y
 constexpr int kOutHC = 2;    // y and hCache
 
-template <int DISC, int KS, int NS>
+// DN: every activation row stride is D and the B/C stride is N (dense
+// tensors); the strides then fold into one row offset per step.
+template <int DISC, int KS, int NS, bool DN>
 struct Scan {
     using L_t = Lane<KS, NS>;
     static constexpr int NR = L_t::NR;
@@ -90,6 +92,7 @@ struct Scan {
     const int N, K;
     const uint32_t d;       // this lane's channel, clamped to D-1
     const int64_t b;
+    const int64_t ldx, ldz, ldd, ldB, ldC, ldy;   // row strides (elements)
     const float* zsrc;      // z, or any valid array when ungated
     const bool gated;
     float4* lds;            // 64 float4 for this wave: B rows [0, 32), C rows [32, 64)
@@ -99,11 +102,14 @@ struct Scan {
     __device__ Scan(const Cols& c_, const ScanShape& s, int64_t b_, int64_t d_raw, float4* lds_)
         : c(c_), L(s.L), D(s.D), N(NS > 0 ? NS : s.N), K(KS > 0 ? KS : s.K),
           d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)), b(b_),
+          ldx(DN ? s.D : s.ld_src), ldz(DN ? s.D : (c_.z ? s.ld_z : s.ld_src)),
+          ldd(DN ? s.D : s.ld_delta), ldB(DN ? N : s.ld_B), ldC(DN ? N : s.ld_C),
+          ldy(DN ? s.D : s.ld_y),
           zsrc(c_.z ? c_.z : c_.src), gated(c_.z != nullptr), lds(lds_) {}
 
     __device__ __forceinline__ int64_t row(int64_t t) const { return b * L + t; }
-    __device__ __forceinline__ float ld(const float* base, int64_t t) const {
-        return (base + row(t) * D)[d];
+    __device__ __forceinline__ float ld(const float* base, int64_t stride, int64_t t) const {
+        return (base + row(t) * stride)[d];
     }
 
     __device__ __forceinline__ void init(L_t& ln) const {
@@ -140,7 +146,7 @@ struct Scan {
 #pragma unroll
             for (int i = 0; i < kBackBlk; i++) {
                 const int64_t tt = t - 1 - i;
-                dd[i] = ld(c.delta, tt >= 0 ? tt : 0);
+                dd[i] = ld(c.delta, ldd, tt >= 0 ? tt : 0);
             }
 #pragma unroll
             for (int i = 0; i < kBackBlk; i++) {
@@ -158,7 +164,7 @@ struct Scan {
 #pragma unroll
             for (int j = 0; j < KR - 1; j++) {
                 const int64_t tt = t - 1 - j;
-                ln.xw[j] = (j < K - 1 && tt >= 0) ? ld(c.src, tt) : 0.0f;
+                ln.xw[j] = (j < K - 1 && tt >= 0) ? ld(c.src, ldx, tt) : 0.0f;
             }
         }
     }
@@ -171,9 +177,9 @@ struct Scan {
 #pragma unroll
         for (int i = 0; i < kT; i++) {
             const int64_t t = t0 + i < L ? t0 + i : L - 1;
-            xs[i] = ld(c.src, t);
-            ds[i] = ld(c.delta, t);
-            if constexpr (OUT != kWarm) zs[i] = ld(zsrc, t);
+            xs[i] = ld(c.src, ldx, t);
+            ds[i] = ld(c.delta, ldd, t);
+            if constexpr (OUT != kWarm) zs[i] = ld(zsrc, ldz, t);
         }
     }
 
@@ -184,8 +190,8 @@ struct Scan {
         const uint32_t q = lane & 31u;
         int64_t t = t0 + (q >> 2);
         t = t < L ? t : L - 1;
-        const float* base = lane < 32 ? c.Bm : c.Cm;
-        return *reinterpret_cast<const float4*>(base + row(t) * 16 + (q & 3u) * 4);
+        const float* base = lane < 32 ? c.Bm + row(t) * ldB : c.Cm + row(t) * ldC;
+        return *reinterpret_cast<const float4*>(base + (q & 3u) * 4);
     }
 
     // One time step.  SLOW: some lane has |dv A| < 2^-6 (see below).
@@ -219,8 +225,8 @@ struct Scan {
                 }
             }
         } else {
-            const cfloat* Br = as_const(c.Bm + row(t) * N);
-            const cfloat* Cr = as_const(c.Cm + row(t) * N);
+            const cfloat* Br = as_const(c.Bm + row(t) * ldB);
+            const cfloat* Cr = as_const(c.Cm + row(t) * ldC);
 #pragma unroll
             for (int n = 0; n < NR; n++) {
                 Bv[n] = (NS > 0 || n < N) ? Br[n] : 0.0f;
@@ -281,7 +287,7 @@ struct Scan {
         if constexpr (OUT != kWarm) {
             const int64_t r = row(t);
             const float g = silu(zv);
-            (c.y + r * D)[d] = gated ? yv * g : yv;
+            (c.y + r * ldy)[d] = gated ? yv * g : yv;
             if constexpr (OUT == kOutHC) {
                 float* __restrict__ hc = c.h_cache + r * D * N;
                 if constexpr (NS > 0 && NS % 4 == 0) {
@@ -306,9 +312,9 @@ struct Scan {
     __device__ __forceinline__ void steps1(L_t& ln, int64_t t0, int cnt) const {
         for (int i = 0; i < cnt; i++) {
             const int64_t t = t0 + i;
-            const float xv = ld(c.src, t);
-            const float dv = softplus(ld(c.delta, t));
-            const float zv = OUT != kWarm ? ld(zsrc, t) : 0.0f;
+            const float xv = ld(c.src, ldx, t);
+            const float dv = softplus(ld(c.delta, ldd, t));
+            const float zv = OUT != kWarm ? ld(zsrc, ldz, t) : 0.0f;
             if (!wave_any(dv * ln.min_a2 < kSmallX2))
                 step<OUT, false, LDS>(ln, xv, dv, zv, t, i);
             else
@@ -388,8 +394,11 @@ struct Scan {
     }
 };
 
-template <int DISC, int KS, int NS>
-__global__ __launch_bounds__(kWave) void scan_kernel(Cols c, ScanShape s) {
+// Two waves per SIMD: one wave alone issues VALU work only about every other
+// slot, so the register budget is capped at 256 VGPRs.
+template <int DISC, int KS, int NS, bool DN>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_kernel(
+    Cols c, ScanShape s) {
     __shared__ float4 lds[kWave];
     const int64_t lane = threadIdx.x;
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * s.seg;
@@ -402,23 +411,26 @@ __global__ __launch_bounds__(kWave) void scan_kernel(Cols c, ScanShape s) {
         const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
         const int64_t b = tile / s.tiles_per_b;
         const int64_t dt = tile - b * s.tiles_per_b;
-        Scan<DISC, KS, NS> sc(c, s, b, dt * kWave + lane, lds);
+        Scan<DISC, KS, NS, DN> sc(c, s, b, dt * kWave + lane, lds);
         sc.run(t0, t1);
         g += t1 - t0;
     }
 }
 
-template <int DISC, int KS, int NS>
+template <int DISC, int KS, int NS, bool DN>
 hipError_t launch_t(const Cols& c, const ScanShape& s, hipStream_t st) {
     const int64_t nblk = (s.total + s.seg - 1) / s.seg;
-    hipLaunchKernelGGL((scan_kernel<DISC, KS, NS>), dim3(static_cast<unsigned>(nblk)),
+    hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN>), dim3(static_cast<unsigned>(nblk)),
                        dim3(kWave), 0, st, c, s);
     return hipGetLastError();
 }
 
 template <int DISC, int KS>
 hipError_t launch_n(const Cols& c, const ScanShape& s, hipStream_t st) {
-    return s.N == 16 ? launch_t<DISC, KS, 16>(c, s, st) : launch_t<DISC, KS, 0>(c, s, st);
+    if (s.N == 16 && s.bc_vec)
+        return s.dense ? launch_t<DISC, KS, 16, true>(c, s, st)
+                       : launch_t<DISC, KS, 16, false>(c, s, st);
+    return launch_t<DISC, KS, 0, false>(c, s, st);
 }
 
 template <int DISC>

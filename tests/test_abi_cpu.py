@@ -150,3 +150,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mss, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         mss.lib()
+
+
+def core_strided(L, dims, strides, **over):
+    args = dict(x=fake(1), w_conv=fake(2), b_conv=None, delta=fake(3), A_log=fake(4), B=fake(5),
+                C=fake(6), D_vec=fake(7), z=fake(8), h0=None, y=fake(9), h_cache=None,
+                h_last=None)
+    args.update(over)
+    s = ctypes.byref(strides) if strides is not None else None
+    return L.mss_mamba1_core_strided(ctypes.byref(dims), s, 0, *args.values(), None)
+
+
+def test_strided_validation(L):
+    d = mss.make_dims(2, 16, 64, 16, 4)
+    ok = mss.make_strides(128, 128, 64, 48, 48, 64)
+    assert core_strided(L, d, None) == EINVAL
+    bad = mss.make_strides(128, 128, 64, 48, 48, 64)
+    bad.struct_size = 8
+    assert core_strided(L, d, bad) == EINVAL
+    for field, width in (("x", 64), ("z", 64), ("delta", 64), ("B", 16), ("C", 16), ("y", 64)):
+        s = mss.make_strides(128, 128, 64, 48, 48, 64)
+        setattr(s, field, width - 1)               # row stride below the row width
+        assert core_strided(L, d, s) == EINVAL, field
+    # activations may be 4-byte aligned in the strided call: the call gets past
+    # the alignment checks and is rejected only for y overlapping x
+    x4 = ctypes.c_void_p(BASE + 1 * (1 << 32) + 4)
+    assert core_strided(L, d, ok, x=x4, y=ctypes.c_void_p(BASE + (1 << 32) + 64)) == EALIAS
+    # the dense call keeps the 16-byte rule for the same pointer
+    dense = [x4, fake(2), None, fake(3), fake(4), fake(5), fake(6), fake(7), fake(8), None,
+             fake(9), None, None]
+    assert L.mss_mamba1_core(ctypes.byref(d), 0, *dense, None) == EALIGN
+    # state tensors keep the 16-byte rule in the strided call
+    assert core_strided(L, d, ok, h0=ctypes.c_void_p(BASE + 10 * (1 << 32) + 8)) == EALIGN
+    # x and z as interleaved halves of one (M, 2D) buffer are fine (both inputs);
+    # y inside that buffer's span is not
+    xz = BASE + 11 * (1 << 32)
+    s = mss.make_strides(128, 128, 64, 48, 48, 64)
+    assert core_strided(L, d, s, x=ctypes.c_void_p(xz), z=ctypes.c_void_p(xz + 256),
+                        y=ctypes.c_void_p(xz + 128 * 4 * 5)) == EALIAS
+    # empty problem: nothing to launch
+    d0 = mss.make_dims(2, 16, 0, 16, 4)
+    assert L.mss_selective_scan_strided(ctypes.byref(d0), ctypes.byref(ok), 1, None, None, None,
+                                        fake(5), fake(6), None, None, None, None, None, None,
+                                        None) == 0

@@ -319,3 +319,44 @@ def test_steps_match_sequence(disc):
         ys.append(host(y))
         assert_close(host(h), hc[:, t], f"h at t={t}")
     assert_close(np.stack(ys, 1).reshape(B * L, D), y_seq, "y")
+
+
+# ---------------------------------------------------------------------------
+# strided inputs: column slices of the projection outputs, read in place
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("R", (48, 5), ids=("bc_aligned", "bc_unaligned"))
+@pytest.mark.parametrize("entry", ("core", "scan"))
+def test_strided_column_slices(entry, R, disc):
+    import torch
+    w = gen.SMALL.with_(name="strided", batch=2, seq_len=1500, d_inner=192, hcache=True)
+    inp = gen.generate(w, seed_offset=14)
+    M, D, N, B, L = w.M, w.d_inner, w.d_state, w.batch, w.seq_len
+    g = np.random.default_rng(15)
+    junk = lambda c: g.standard_normal((M, c)).astype(np.float32)
+    XZ = dev(np.concatenate([inp["x"], inp["z"]], axis=1))                 # (M, 2D)
+    XP = dev(np.concatenate([junk(R), inp["B"], inp["C"]], axis=1))       # (M, R+2N)
+    DP = dev(np.concatenate([inp["delta"], junk(5)], axis=1))             # (M, D+5)
+    YB = nan_like((M, D + 7))
+    x, z = XZ[:, :D], XZ[:, D:]
+    Bv, Cv = XP[:, R:R + N], XP[:, R + N:]
+    dl, y = DP[:, :D], YB[:, 3:3 + D]
+    hc, hl = nan_like((B, L, D, N)), nan_like((B, D, N))
+    d = {k: dev(inp[k]) for k in ("w_conv", "b_conv", "A_log", "D_vec")}
+    if entry == "core":
+        mss.mamba1_core(x, d["w_conv"], d["b_conv"], dl, d["A_log"], Bv, Cv, d["D_vec"], z, None,
+                        batch=B, seq_len=L, disc=disc, h_cache=hc, h_last=hl, out=y)
+        oy, ohc, ohl = oracle_core(inp, w, disc)
+    else:
+        mss.selective_scan(x, dl, d["A_log"], Bv, Cv, d["D_vec"], z, None, batch=B, seq_len=L,
+                           disc=disc, h_cache=hc, h_last=hl, out=y)
+        oy, ohc, ohl = oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"],
+                                             inp["C"], inp["D_vec"], inp["z"], None, batch=B,
+                                             seq_len=L, disc=disc, h_cache=True, h_last=True)
+    torch.cuda.synchronize()
+    assert_close(host(y), oy, "y")
+    assert_close(host(hc), ohc, "h_cache")
+    assert_close(host(hl), ohl, "h_last")
+    outside = torch.cat([YB[:, :3], YB[:, 3 + D:]], dim=1)
+    assert torch.isnan(outside).all().item(), "wrote outside the y slice"
