@@ -60,8 +60,11 @@ def _declare(lib):
                                        p, p, p, i64, p, p, p, i32]
     lib.oracle_selective_step.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, p,
                                           p, p, p, i64, p, p, p, i32]
+    lib.oracle_selective_scan_backward.argtypes = [i64, i64, i64, i64, i32] + [p] * 17 + [i32]
+    lib.oracle_conv1d_silu_backward.argtypes = [i64, i64, i64, i64] + [p] * 7 + [i32]
     for f in (lib.oracle_conv1d_silu, lib.oracle_selective_scan, lib.oracle_mamba1_core,
-              lib.oracle_selective_step):
+              lib.oracle_selective_step, lib.oracle_selective_scan_backward,
+              lib.oracle_conv1d_silu_backward):
         f.restype = ctypes.c_int
     return lib
 
@@ -201,6 +204,48 @@ def selective_step(x, z, delta, A_log, B, C, D_vec, w_conv, b_conv, conv_state, 
     return y, cs_out, h_out
 
 
+def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch, seq_len, disc,
+                            nthreads=0, lib=None):
+    """Gradients of the gated scan output against ``dout`` (fp64 dict).
+
+    Keys: du, ddelta, dz (or None when z is None) (M, D); dA_log (D, N);
+    dB, dC (M, N); dD (D,); dh0 (batch, D, N).  ``du`` is the gradient that
+    reaches u through the scan only.
+    """
+    Dn, N = A_log.shape
+    M = batch * seq_len
+    args = [_f32(u, "u", (M, Dn)), _f32(delta, "delta", (M, Dn)), _f32(A_log, "A_log", (Dn, N)),
+            _f32(B, "B", (M, N)), _f32(C, "C", (M, N)), _f32(D_vec, "D_vec", (Dn,)),
+            _f32(z, "z", (M, Dn)), _f32(h0, "h0", (batch, Dn, N)),
+            _f32(dout, "dout", (M, Dn))]
+    out = {"du": np.empty((M, Dn)), "ddelta": np.empty((M, Dn)), "dA_log": np.empty((Dn, N)),
+           "dB": np.empty((M, N)), "dC": np.empty((M, N)), "dD": np.empty((Dn,)),
+           "dz": np.empty((M, Dn)) if z is not None else None,
+           "dh0": np.empty((batch, Dn, N))}
+    rc = (lib or load()).oracle_selective_scan_backward(
+        batch, seq_len, Dn, N, _disc(disc), *map(_ptr, args),
+        *(_ptr(out[k]) for k in ("du", "ddelta", "dA_log", "dB", "dC", "dD", "dz", "dh0")),
+        nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan_backward failed ({rc})")
+    return out
+
+
+def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, nthreads=0, lib=None):
+    """Gradients of u = SiLU(conv1d(x)) against ``du``: (dx, dw_conv, db_conv), fp64."""
+    D = x.shape[-1]
+    K = w_conv.shape[1]
+    M = batch * seq_len
+    args = [_f32(x, "x", (M, D)), _f32(w_conv, "w_conv", (D, K)), _f32(b_conv, "b_conv", (D,)),
+            _f32(du, "du", (M, D))]
+    dx, dw, db = np.empty((M, D)), np.empty((D, K)), np.empty((D,))
+    rc = (lib or load()).oracle_conv1d_silu_backward(batch, seq_len, D, K, *map(_ptr, args),
+                                                     _ptr(dx), _ptr(dw), _ptr(db), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d_silu_backward failed ({rc})")
+    return dx, dw, db
+
+
 class Bound:
     """The same API bound to one specific oracle build (used by the tests that
     check the pins against deliberately broken copies of ``oracle.c``)."""
@@ -219,6 +264,12 @@ class Bound:
 
     def selective_step(self, *a, **k):
         return selective_step(*a, lib=self.lib, **k)
+
+    def selective_scan_backward(self, *a, **k):
+        return selective_scan_backward(*a, lib=self.lib, **k)
+
+    def conv1d_silu_backward(self, *a, **k):
+        return conv1d_silu_backward(*a, lib=self.lib, **k)
 
 
 def default() -> Bound:

@@ -15,8 +15,9 @@
  * Source of every formula: the pages of the npm package
  * "@seanhogg/builderforce-memory-engine", in particular the diff
  * 2026.7.12 -> 2026.9.27, file src/training/mamba1_cpu.ts, function
- * mamba1CpuForward (steps 4, 5, 8 and 9), and the diff 2026.7.14 -> 2026.9.28,
- * file src/training/cpu_ops.ts (silu, softplus).  Layouts are the ones that
+ * mamba1CpuForward (steps 4, 5, 8 and 9) and mamba1CpuBackward (the gate,
+ * the reverse-time scan adjoint, softplus, SiLU and conv1d parts), and the
+ * diff 2026.7.14 -> 2026.9.28, file src/training/cpu_ops.ts (silu, softplus).  Layouts are the ones that
  * file's header lists: activations (M, D) with M = batch * seqLen and row
  * r = b * seqLen + t, B and C (M, N), A_log (D, N), wConv (D, K),
  * hCache (B, L, D, N).
@@ -279,6 +280,249 @@ int oracle_selective_step(int64_t B, int64_t D, int64_t N, int64_t K, int disc,
             if (cols) conv_state_out[i * S + j] = nv;
             else conv_state_out[(b * S + j) * D + d] = nv;
         }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass of steps 8 + 9 (the scan and the gate), from the reverse-time
+ * adjoint in the same diff's mamba1CpuBackward ("Selective scan, walked
+ * backwards in time", and the gate and softplus parts around it).  Given the
+ * gradient dout of the gated output:
+ *   dY = dout * silu(z)                 dz = dout * y * silu'(z)   (y ungated)
+ *   dD_vec[d] += dY * u                 du = dY * D_vec[d] + sum_n dh_n * bBar_n
+ *   dh_n  = dY * C[r,n] + g_n           (g_n = dL/dh_t carried from step t+1)
+ *   dC[r,n] += dY * h_t,n               dB[r,n] += dh_n * u * dbBar/dB
+ *   g_n  <- dh_n * aBar_n               (flows to step t-1)
+ *   ddv  = sum_n dh_n h_{t-1,n} A_n aBar_n + dh_n u dbBar/ddv
+ *   dA_n += dh_n h_{t-1,n} dv aBar_n + dh_n u dbBar/dA
+ *   ddelta = ddv * sigmoid(delta)       dA_log = dA * A inside the clamp, else 0
+ *   dh0 = g after step 0
+ * with, for ZOH bBar = expm1(dv A)/A * B:
+ *   dbBar/dB = expm1(dv A)/A,  dbBar/ddv = aBar B,
+ *   dbBar/dA = B (dv A aBar - expm1(dv A)) / A^2   (written as B dv^2 phi(dv A)
+ *   with phi(x) = (x e^x - expm1(x)) / x^2, a series for small |x|, so the
+ *   difference does not cancel), and for EULER bBar = dv B:
+ *   dbBar/dB = dv, dbBar/ddv = B, dbBar/dA = 0.
+ * The clamp boundary itself counts as outside (zero gradient), as on the pages. */
+static double phi_zoh(double x) {
+    if (fabs(x) < 1e-2) {
+        /* sum_{k>=2} (k-1)/k! x^(k-2) */
+        double term = 0.0, xp = 1.0, fact = 2.0;
+        for (int k = 2; k < 12; k++) {
+            term += (double)(k - 1) / fact * xp;
+            xp *= x;
+            fact *= (double)(k + 1);
+        }
+        return term;
+    }
+    return (x * exp(x) - expm1(x)) / (x * x);
+}
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* d silu / dv = s (1 + v (1 - s)),  s = sigmoid(v). */
+static double silu_grad(double v) {
+    const double s = sigmoid(v);
+    return s * (1.0 + v * (1.0 - s));
+}
+
+typedef struct {
+    int64_t B, L, D, N;
+    int disc;
+    const float *u, *delta, *A_log, *Bm, *Cm, *Dv, *z, *h0, *dout;
+} bwd_args;
+
+/* One (b, d) column.  hs holds (L + 1) * N states (h_{-1} .. h_{L-1}).
+ * Column-local outputs go straight to du, ddelta, dz, dh0; the cross-column
+ * sums are written per column (dB_col, dC_col: L * N; dA_col: N; dD_col: 1)
+ * and reduced afterwards in a fixed order.                                  */
+static void scan_column_bwd(const bwd_args* a, int64_t b, int64_t d, double* hs, double* ys,
+                            double* du, double* ddelta, double* dz, double* dh0,
+                            double* dB_col, double* dC_col, double* dA_col, double* dD_col) {
+    const int64_t L = a->L, D = a->D, N = a->N;
+    double A[ORACLE_MAX_N], g[ORACLE_MAX_N], dA[ORACLE_MAX_N];
+    for (int64_t n = 0; n < N; n++) {
+        A[n] = a_cont((double)a->A_log[d * N + n]);
+        hs[n] = a->h0 ? (double)a->h0[(b * D + d) * N + n] : 0.0;
+        g[n] = 0.0;
+        dA[n] = 0.0;
+    }
+    const double Dd = a->Dv ? (double)a->Dv[d] : 0.0;
+    /* Forward: the states and the ungated output of every step. */
+    for (int64_t t = 0; t < L; t++) {
+        const int64_t r = b * L + t;
+        const double dv = softplus((double)a->delta[r * D + d]);
+        const double uv = (double)a->u[r * D + d];
+        double yv = Dd * uv;
+        for (int64_t n = 0; n < N; n++) {
+            const double ab = exp(dv * A[n]);
+            const double bb = b_bar(a->disc, dv, A[n], (double)a->Bm[r * N + n]);
+            hs[(t + 1) * N + n] = ab * hs[t * N + n] + bb * uv;
+            yv += (double)a->Cm[r * N + n] * hs[(t + 1) * N + n];
+        }
+        ys[t] = yv;
+    }
+    /* Reverse. */
+    double dDsum = 0.0;
+    for (int64_t t = L - 1; t >= 0; t--) {
+        const int64_t r = b * L + t;
+        const double dl = (double)a->delta[r * D + d];
+        const double dv = softplus(dl);
+        const double uv = (double)a->u[r * D + d];
+        const double go = (double)a->dout[r * D + d];
+        double dY = go;
+        if (a->z) {
+            const double zv = (double)a->z[r * D + d];
+            dY = go * silu(zv);
+            dz[r * D + d] = go * ys[t] * silu_grad(zv);
+        }
+        dDsum += dY * uv;
+        double duv = dY * Dd;
+        double ddv = 0.0;
+        for (int64_t n = 0; n < N; n++) {
+            const double Bv = (double)a->Bm[r * N + n];
+            const double Cv = (double)a->Cm[r * N + n];
+            const double x = dv * A[n];
+            const double ab = exp(x);
+            const double hprev = hs[t * N + n];
+            const double hcur = hs[(t + 1) * N + n];
+            dC_col[t * N + n] = dY * hcur;
+            const double dh = dY * Cv + g[n];
+            const double dab = dh * hprev;      /* dL/d aBar */
+            const double dbb = dh * uv;         /* dL/d bBar */
+            duv += dh * b_bar(a->disc, dv, A[n], Bv);
+            g[n] = dh * ab;
+            if (a->disc == ORACLE_DISC_ZOH) {
+                ddv += dab * A[n] * ab + dbb * ab * Bv;
+                dA[n] += dab * dv * ab + dbb * Bv * dv * dv * phi_zoh(x);
+                dB_col[t * N + n] = dbb * expm1(x) / A[n];
+            } else {
+                ddv += dab * A[n] * ab + dbb * Bv;
+                dA[n] += dab * dv * ab;
+                dB_col[t * N + n] = dbb * dv;
+            }
+        }
+        du[r * D + d] = duv;
+        ddelta[r * D + d] = ddv * sigmoid(dl);
+    }
+    for (int64_t n = 0; n < N; n++) {
+        const double al = (double)a->A_log[d * N + n];
+        dA_col[n] = (al <= A_LOG_LO || al >= A_LOG_HI) ? 0.0 : dA[n] * A[n];
+        if (dh0) dh0[(b * D + d) * N + n] = g[n];
+    }
+    *dD_col = dDsum;
+}
+
+/* Outputs (all fp64, dense): du, ddelta, dz (B*L, D); dA_log (D, N);
+ * dB, dC (B*L, N); dD (D); dh0 (B, D, N).  dz may be NULL when z is NULL;
+ * dh0 may be NULL.                                                          */
+int oracle_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int disc,
+                                   const float* u, const float* delta, const float* A_log,
+                                   const float* Bm, const float* Cm, const float* Dv,
+                                   const float* z, const float* h0, const float* dout,
+                                   double* du, double* ddelta, double* dA_log, double* dB,
+                                   double* dC, double* dD, double* dz, double* dh0,
+                                   int nthreads) {
+    if (B < 0 || L < 0 || D < 0 || N < 1 || N > ORACLE_MAX_N) return -1;
+    if (disc != ORACLE_DISC_ZOH && disc != ORACLE_DISC_EULER) return -1;
+    if (!u || !delta || !A_log || !Bm || !Cm || !dout) return -1;
+    if (!du || !ddelta || !dA_log || !dB || !dC || !dD) return -1;
+    if (z && !dz) return -1;
+    bwd_args a = {B, L, D, N, disc, u, delta, A_log, Bm, Cm, Dv, z, h0, dout};
+    const int64_t cols = B * D;
+    double* colB = (double*)calloc((size_t)(cols * L * N + 1), sizeof(double));
+    double* colC = (double*)calloc((size_t)(cols * L * N + 1), sizeof(double));
+    double* colA = (double*)calloc((size_t)(cols * N + 1), sizeof(double));
+    double* colD = (double*)calloc((size_t)(cols + 1), sizeof(double));
+    if (!colB || !colC || !colA || !colD) {
+        free(colB); free(colC); free(colA); free(colD);
+        return -2;
+    }
+    int nt = set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+        double* ys = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        if (!hs || !ys) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t c = 0; c < cols; c++) {
+            if (!hs || !ys) continue;
+            const int64_t b = c / D, d = c % D;
+            scan_column_bwd(&a, b, d, hs, ys, du, ddelta, dz, dh0, colB + c * L * N,
+                            colC + c * L * N, colA + c * N, colD + c);
+        }
+        free(hs);
+        free(ys);
+    }
+    if (err == 0) {
+        /* Cross-column sums in a fixed order: over d for dB, dC; over b for
+         * dA_log, dD. */
+#pragma omp parallel for schedule(static) num_threads(nt)
+        for (int64_t i = 0; i < B * L * N; i++) {
+            const int64_t b = i / (L * N), tn = i % (L * N);
+            double sb = 0.0, sc = 0.0;
+            for (int64_t d = 0; d < D; d++) {
+                sb += colB[(b * D + d) * L * N + tn];
+                sc += colC[(b * D + d) * L * N + tn];
+            }
+            dB[i] = sb;
+            dC[i] = sc;
+        }
+        for (int64_t i = 0; i < D * N; i++) {
+            const int64_t d = i / N, n = i % N;
+            double s = 0.0;
+            for (int64_t b = 0; b < B; b++) s += colA[(b * D + d) * N + n];
+            dA_log[i] = s;
+        }
+        for (int64_t d = 0; d < D; d++) {
+            double s = 0.0;
+            for (int64_t b = 0; b < B; b++) s += colD[b * D + d];
+            dD[d] = s;
+        }
+    }
+    free(colB); free(colC); free(colA); free(colD);
+    return err;
+}
+
+/* Backward of steps 4 + 5 (the same diff's mamba1CpuBackward, "SiLU" and
+ * "Depthwise causal conv1d"): with c the conv output and dc = du * silu'(c),
+ *   dx[b, t-k, d] += dc[b,t,d] * wConv[d,k]   (t >= k)
+ *   dwConv[d,k]   += dc[b,t,d] * x[b, t-k, d]
+ *   dbConv[d]     += dc[b,t,d]
+ * du is the total gradient reaching u.  Outputs fp64: dx (B*L, D),
+ * dw (D, K), db (D).                                                        */
+int oracle_conv1d_silu_backward(int64_t B, int64_t L, int64_t D, int64_t K,
+                                const float* x, const float* w, const float* bias,
+                                const float* du, double* dx, double* dw, double* db,
+                                int nthreads) {
+    if (B < 0 || L < 0 || D < 0 || K < 1 || K > ORACLE_MAX_K) return -1;
+    if (!x || !w || !du || !dx || !dw || !db) return -1;
+    int nt = set_threads(nthreads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t d = 0; d < D; d++) {
+        double sw[ORACLE_MAX_K];
+        double sb = 0.0;
+        for (int64_t k = 0; k < K; k++) sw[k] = 0.0;
+        for (int64_t b = 0; b < B; b++) {
+            for (int64_t t = 0; t < L; t++) dx[(b * L + t) * D + d] = 0.0;
+            for (int64_t t = 0; t < L; t++) {
+                const int64_t r = b * L + t;
+                const double dc = (double)du[r * D + d] *
+                                  silu_grad(conv_at(x, w, bias, L, D, K, b, t, d));
+                sb += dc;
+                for (int64_t k = 0; k < K && k <= t; k++) {
+                    sw[k] += dc * (double)x[(r - k) * D + d];
+                    dx[(r - k) * D + d] += dc * (double)w[d * K + k];
+                }
+            }
+        }
+        for (int64_t k = 0; k < K; k++) dw[d * K + k] = sw[k];
+        db[d] = sb;
     }
     return 0;
 }

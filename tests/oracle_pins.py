@@ -507,4 +507,142 @@ def pin_step_from_carried_state(orc):
     _close(yt, y.reshape(Bt, L, D)[:, p], 1e-13, 1e-15, "step after prefix")
 
 
+# --------------------------------------------------------------------------
+# Backward passes: pinned to central finite differences of the (separately
+# pinned) forward oracle, and to a closed form evaluated in 60-digit decimal
+# arithmetic.
+
+_BWD_INPUTS = ("u", "delta", "A_log", "B", "C", "D_vec", "z", "h0")
+_GRAD_OF = {"u": "du", "delta": "ddelta", "A_log": "dA_log", "B": "dB", "C": "dC",
+            "D_vec": "dD", "z": "dz", "h0": "dh0"}
+
+
+def _fd_element(f, arr, idx, rel=2.0 ** -11):
+    """Central difference of f at arr[idx], on the fp32 grid: both perturbed
+    values are fp32 numbers and the step is their exact difference."""
+    v = float(arr[idx])
+    step = rel * max(abs(v), 0.25)
+    hi, lo = np.float32(v + step), np.float32(v - step)
+    arr[idx] = hi
+    fp = f()
+    arr[idx] = lo
+    fm = f()
+    arr[idx] = np.float32(v)
+    return (fp - fm) / (float(hi) - float(lo))
+
+
+def _scan_loss(orc, inp, dout, B, L, disc):
+    def f():
+        y, _, _ = orc.selective_scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"],
+                                     inp["D_vec"], inp["z"], inp["h0"], batch=B, seq_len=L,
+                                     disc=disc)
+        return float(np.sum(y * dout))
+    return f
+
+
+def _check_scan_grads(orc, inp, dout, B, L, disc, picks=None, rtol=2e-5):
+    g = orc.selective_scan_backward(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"],
+                                    inp["D_vec"], inp["z"], inp["h0"], dout, batch=B,
+                                    seq_len=L, disc=disc)
+    f = _scan_loss(orc, inp, dout, B, L, disc)
+    rs = _rng(99)
+    for name in _BWD_INPUTS:
+        arr = inp[name]
+        grad = g[_GRAD_OF[name]].reshape(arr.shape)
+        scale = float(np.sqrt(np.mean(grad ** 2))) + 1e-30
+        idxs = list(np.ndindex(arr.shape))
+        if picks is not None and len(idxs) > picks:
+            idxs = [idxs[i] for i in rs.choice(len(idxs), picks, replace=False)]
+        for idx in idxs:
+            fd = _fd_element(f, arr, idx)
+            assert abs(fd - grad[idx]) <= rtol * (abs(grad[idx]) + scale), (
+                f"{disc} d/d{name}{idx}: oracle {grad[idx]:.10e} vs finite difference {fd:.10e}")
+
+
+def pin_scan_backward_finite_differences(orc):
+    # Every element of every input, both modes; A_log has entries on both
+    # sides of the clamp (their gradient must be exactly zero).
+    B, L, D, N = 2, 6, 3, 4
+    for disc in (ZOH, EULER):
+        inp = _scan_inputs(31, B, L, D, N, alog_lo=-2.0, alog_hi=1.5)
+        inp["A_log"][0, 1] = -11.5
+        inp["A_log"][2, 3] = 5.75
+        dout = _f32(_rng(32).standard_normal((B * L, D)))
+        _check_scan_grads(orc, inp, dout, B, L, disc)
+        g = orc.selective_scan_backward(inp["u"], inp["delta"], inp["A_log"], inp["B"],
+                                        inp["C"], inp["D_vec"], inp["z"], inp["h0"], dout,
+                                        batch=B, seq_len=L, disc=disc)
+        assert g["dA_log"][0, 1] == 0.0 and g["dA_log"][2, 3] == 0.0
+
+
+def pin_scan_backward_long_memory(orc):
+    # Slow decay (small dv, small |A|), so gradients of early steps travel
+    # through the carried adjoint across the whole sequence; no gate, no h0.
+    B, L, D, N = 1, 48, 2, 3
+    for disc in (ZOH, EULER):
+        inp = _scan_inputs(41, B, L, D, N, alog_lo=-3.0, alog_hi=-1.0, delta_mu=-2.0)
+        inp["z"] = None
+        inp["h0"] = None
+        dout = _f32(_rng(42).standard_normal((B * L, D)))
+        g = orc.selective_scan_backward(inp["u"], inp["delta"], inp["A_log"], inp["B"],
+                                        inp["C"], inp["D_vec"], None, None, dout, batch=B,
+                                        seq_len=L, disc=disc)
+        assert g["dz"] is None
+        f = _scan_loss(orc, inp, dout, B, L, disc)
+        for name, idx in (("u", (0, 0)), ("u", (3, 1)), ("delta", (1, 0)), ("delta", (2, 1)),
+                          ("B", (0, 2)), ("B", (1, 0)), ("A_log", (0, 0)), ("A_log", (1, 2)),
+                          ("C", (47, 1)), ("D_vec", (1,))):
+            arr = inp[name]
+            grad = g[_GRAD_OF[name]].reshape(arr.shape)
+            fd = _fd_element(f, arr, idx)
+            assert abs(fd - grad[idx]) <= 2e-5 * (abs(grad[idx]) + 1e-3), (
+                f"{disc} long d/d{name}{idx}: {grad[idx]:.10e} vs {fd:.10e}")
+
+
+def pin_zoh_a_grad_tiny_step_closed_form(orc):
+    # L = 1, h0 = 0, one state, ungated, no skip: y = C u B expm1(dv A) / A,
+    # so dy/dA_log = C u B (x e^x - expm1(x)) / A with x = dv A, A = -e^A_log.
+    # Evaluated in 60-digit decimal arithmetic, for |x| from 1e-9 to 1.
+    import decimal
+    ctx = decimal.Context(prec=60)
+    Dm = decimal.Decimal
+    for delta, alog in ((-20.0, 0.3), (-9.0, -1.0), (-4.0, 0.5), (0.5, 0.0), (-1.0, 1.2)):
+        u = _f32([[1.25]])
+        dl = _f32([[delta]])
+        al = _f32([[alog]])
+        Bm, Cm = _f32([[0.75]]), _f32([[-1.5]])
+        dout = _f32([[1.0]])
+        g = orc.selective_scan_backward(u, dl, al, Bm, Cm, None, None, None, dout, batch=1,
+                                        seq_len=1, disc=ZOH)
+        dd = Dm(float(dl[0, 0]))
+        dv = ctx.add(max(dd, Dm(0)), ctx.ln(ctx.add(Dm(1), ctx.exp(-abs(dd)))))
+        A = -ctx.exp(Dm(float(al[0, 0])))
+        x = ctx.multiply(dv, A)
+        em1 = ctx.subtract(ctx.exp(x), Dm(1))
+        want = (Dm(float(Cm[0, 0])) * Dm(float(u[0, 0])) * Dm(float(Bm[0, 0])) *
+                ctx.divide(ctx.subtract(ctx.multiply(x, ctx.exp(x)), em1), A))
+        got = g["dA_log"][0, 0]
+        assert abs(Dm(got) - want) <= abs(want) * Dm("1e-12"), (
+            f"delta={delta}: {got!r} vs {want}")
+
+
+def pin_conv_backward_finite_differences(orc):
+    Bt, L, D, K = 2, 7, 3, 4
+    g = _rng(51)
+    x = _f32(g.standard_normal((Bt * L, D)))
+    w = _f32(0.5 * g.standard_normal((D, K)))
+    b = _f32(0.3 * g.standard_normal(D))
+    du = _f32(g.standard_normal((Bt * L, D)))
+    dx, dw, db = orc.conv1d_silu_backward(x, w, b, du, batch=Bt, seq_len=L)
+
+    def f():
+        return float(np.sum(orc.conv1d_silu(x, w, b, batch=Bt, seq_len=L) * du))
+    for arr, grad, nm in ((x, dx, "x"), (w, dw, "w"), (b, db, "b")):
+        scale = float(np.sqrt(np.mean(grad ** 2)))
+        for idx in np.ndindex(arr.shape):
+            fd = _fd_element(f, arr, idx)
+            assert abs(fd - grad[idx]) <= 2e-5 * (abs(grad[idx]) + scale), (
+                f"conv d/d{nm}{idx}: oracle {grad[idx]:.10e} vs finite difference {fd:.10e}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,42 @@ MUTANTS = [
     ("step_state_not_shifted", "(j + 1 < S) ? win[j + 1] : xv", "(j + 1 < S) ? win[j] : xv"),
     ("step_dt_ignored_in_input", "const double bb = b_bar(disc, dv, A, (double)Bm[b * N + n]);",
      "const double bb = b_bar(disc, 1.0, A, (double)Bm[b * N + n]);"),
+    # backward of the scan and the gate
+    ("bwd_dab_uses_current_state", "const double dab = dh * hprev;", "const double dab = dh * hcur;"),
+    ("bwd_carry_not_decayed", "g[n] = dh * ab;", "g[n] = dh;"),
+    ("bwd_dC_uses_previous_state", "dC_col[t * N + n] = dY * hcur;",
+     "dC_col[t * N + n] = dY * hprev;"),
+    ("bwd_zoh_ddv_input_term_dropped", "ddv += dab * A[n] * ab + dbb * ab * Bv;",
+     "ddv += dab * A[n] * ab;"),
+    ("bwd_euler_ddv_input_term_decayed", "ddv += dab * A[n] * ab + dbb * Bv;",
+     "ddv += dab * A[n] * ab + dbb * ab * Bv;"),
+    ("bwd_zoh_dA_input_term_dropped",
+     "dA[n] += dab * dv * ab + dbb * Bv * dv * dv * phi_zoh(x);", "dA[n] += dab * dv * ab;"),
+    ("bwd_phi_series_coefficient", "term += (double)(k - 1) / fact * xp;",
+     "term += (double)k / fact * xp;"),
+    ("bwd_zoh_dB_missing_div_a", "dB_col[t * N + n] = dbb * expm1(x) / A[n];",
+     "dB_col[t * N + n] = dbb * expm1(x);"),
+    ("bwd_euler_dB_missing_dv", "dB_col[t * N + n] = dbb * dv;", "dB_col[t * N + n] = dbb;"),
+    ("bwd_gate_grad_is_sigmoid", "dz[r * D + d] = go * ys[t] * silu_grad(zv);",
+     "dz[r * D + d] = go * ys[t] * sigmoid(zv);"),
+    ("bwd_dY_ungated", "dY = go * silu(zv);", "dY = go;"),
+    ("bwd_skip_missing_in_du", "double duv = dY * Dd;", "double duv = 0.0;"),
+    ("bwd_dD_uses_dout", "dDsum += dY * uv;", "dDsum += go * uv;"),
+    ("bwd_softplus_grad_dropped", "ddelta[r * D + d] = ddv * sigmoid(dl);",
+     "ddelta[r * D + d] = ddv;"),
+    ("bwd_clamp_grad_not_zeroed", "(al <= A_LOG_LO || al >= A_LOG_HI) ? 0.0 : dA[n] * A[n]",
+     "dA[n] * A[n]"),
+    ("bwd_dAlog_missing_chain", ": dA[n] * A[n];", ": dA[n];"),
+    ("bwd_h0_not_used", "hs[n] = a->h0 ? (double)a->h0[(b * D + d) * N + n] : 0.0;",
+     "hs[n] = 0.0;"),
+    # backward of conv1d + SiLU
+    ("cbwd_silu_grad_is_sigmoid", "silu_grad(conv_at(x, w, bias, L, D, K, b, t, d))",
+     "sigmoid(conv_at(x, w, bias, L, D, K, b, t, d))"),
+    ("cbwd_dx_taps_reversed", "dx[(r - k) * D + d] += dc * (double)w[d * K + k];",
+     "dx[(r - k) * D + d] += dc * (double)w[d * K + (K - 1 - k)];"),
+    ("cbwd_dw_not_shifted", "sw[k] += dc * (double)x[(r - k) * D + d];",
+     "sw[k] += dc * (double)x[r * D + d];"),
+    ("cbwd_bias_grad_dropped", "db[d] = sb;", "db[d] = 0.0;"),
 ]
 
 
@@ -49,7 +85,10 @@ def src():
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(tmp_path, src, name, old, new):
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    # A text that occurs more than once (e.g. the row index in the forward and
+    # the backward column loops) is mutated everywhere: the same slip made
+    # consistently.
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
     path = tmp_path / "oracle_mut.c"
     path.write_text(src.replace(old, new))
     lib = oracle.load(oracle.build(str(path), str(tmp_path / "liboracle_mut.so")))
