@@ -20,7 +20,7 @@
  *   - All tensor pointers are DEVICE pointers to dense, row-major fp32 arrays
  *     on the current HIP device, allocated and owned by the caller.  The
  *     library allocates nothing, keeps no device state and never frees a
- *     caller buffer.
+ *     caller buffer; the backward passes take a caller workspace.
  *   - Every pointer must be 16-byte aligned (MSS_EALIGN otherwise), except
  *     the activation and B/C tensors of the *_strided entry points (4 bytes).
  *   - Outputs may not overlap any input (MSS_EALIAS), except the state
@@ -54,6 +54,7 @@ extern "C" {
 #define MSS_EINVAL (-1)     /* null required pointer, bad size or limit, bad struct_size, bad disc */
 #define MSS_EALIGN (-2)     /* a pointer is not 16-byte aligned */
 #define MSS_EALIAS (-3)     /* an output overlaps an input */
+#define MSS_EWORKSPACE (-4) /* workspace NULL or smaller than mss_workspace_bytes */
 #define MSS_EHIP (-5)       /* a HIP runtime call or kernel launch failed; see mss_last_hip_error */
 
 /* Problem sizes.  `struct_size` must be sizeof(mss_dims): it guards against a
@@ -163,6 +164,57 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
                        const float* delta, const float* A_log, const float* B, const float* C,
                        const float* D_vec, const float* w_conv, const float* b_conv,
                        float* conv_state, float* h, float* y, hipStream_t stream);
+
+/* ---- Backward passes ------------------------------------------------------
+ * The reverse-time adjoint of the pages' CPU mirror (same diff and file,
+ * function mamba1CpuBackward: the gate, "Selective scan, walked backwards in
+ * time", the A_log clamp mask, softplus, SiLU and the depthwise conv1d).
+ * Gradients are written, not accumulated.  Both entry points take a caller
+ * workspace of at least mss_workspace_bytes bytes for the same dims and
+ * device (256-byte aligned, overlapping nothing else; MSS_EWORKSPACE if
+ * missing or too small); its contents on entry do not matter and it may be
+ * reused once the call's work on `stream` has finished.  Results are
+ * deterministic: every sum runs in a fixed order, no atomics.            */
+
+#define MSS_OP_SELECTIVE_SCAN_BACKWARD 1
+#define MSS_OP_CONV1D_SILU_BACKWARD 2
+
+/* Workspace size in bytes for `op` (one of MSS_OP_*) on the current device;
+ * 0 for empty problems. */
+int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes);
+
+/* Gradients of the selective scan + gate (the forward of mss_selective_scan,
+ * same inputs and layouts) against dout (M, D), the gradient of y:
+ *   dY = dout * SiLU(z) (dout when z is NULL), with h the forward states and
+ *   g the adjoint carried from step t+1, dh = C[r,:] dY + g:
+ *   du (M, D)      = D_vec dY + sum_n dh bBar      (through the scan only:
+ *                    the caller adds what u receives elsewhere)
+ *   ddelta (M, D)  = sigmoid(delta) sum_n (dh h_{t-1} A aBar + dh u dbBar/ddv)
+ *   dA_log (D, N)  = A sum_{b,t} (dh h_{t-1} dv aBar + dh u dbBar/dA),
+ *                    0 where A_log <= -10 or A_log >= 5 (outside the clamp)
+ *   dB, dC (M, N)  = sum_d dh u dbBar/dB,  sum_d dY h_t
+ *   dD_vec (D)     = sum_{b,t} dY u                 (NULL: not computed)
+ *   dz (M, D)      = dout y SiLU'(z), y ungated     (required iff z given)
+ *   dh0 (B, D, N)  = the adjoint after step 0       (NULL: not computed)
+ * The adjoint carried between time segments processed in parallel drops
+ * contributions that have decayed by more than 2^-30, as in the forward.  */
+int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
+                                const float* delta, const float* A_log, const float* B,
+                                const float* C, const float* D_vec, const float* z,
+                                const float* h0, const float* dout, float* du, float* ddelta,
+                                float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
+                                float* dh0, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Gradients of u = SiLU(conv1d(x)) (mss_conv1d_silu) against du (M, D), the
+ * total gradient reaching u:  dc = du * SiLU'(c),
+ *   dx (M, D)         = sum_{k, t+k<L} dc[t+k] w_conv[d,k]
+ *   dw_conv (D, K)    = sum_{b, t>=k} dc[t] x[t-k]
+ *   db_conv (D)       = sum_{b,t} dc[t]            (NULL: not computed)   */
+int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* w_conv,
+                             const float* b_conv, const float* du, float* dx, float* dw_conv,
+                             float* db_conv, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* mss_strerror(int status);

@@ -60,7 +60,11 @@ def make_strides(x, z, delta, B, C, y) -> Strides:
 
 EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_selective_step",
            "mss_selective_scan_strided", "mss_mamba1_core_strided",
+           "mss_workspace_bytes", "mss_selective_scan_backward", "mss_conv1d_silu_backward",
            "mss_strerror", "mss_version", "mss_last_hip_error")
+
+OP_SELECTIVE_SCAN_BACKWARD = 1
+OP_CONV1D_SILU_BACKWARD = 2
 
 _lib = None
 
@@ -82,9 +86,14 @@ def lib():
         sp = ctypes.POINTER(Strides)
         L.mss_selective_scan_strided.argtypes = [dp, sp, i] + [p] * 12
         L.mss_mamba1_core_strided.argtypes = [dp, sp, i] + [p] * 14
+        sz = ctypes.c_size_t
+        L.mss_workspace_bytes.argtypes = [dp, i, ctypes.POINTER(sz)]
+        L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
+        L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
         for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
                   "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
-                  "mss_version", "mss_last_hip_error"):
+                  "mss_workspace_bytes", "mss_selective_scan_backward",
+                  "mss_conv1d_silu_backward", "mss_version", "mss_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         L.mss_strerror.argtypes = [ctypes.c_int]
         L.mss_strerror.restype = ctypes.c_char_p
@@ -271,3 +280,80 @@ def selective_step(x, z, delta, A_log, B, C, D_vec, w_conv, b_conv, conv_state, 
         _ptr(conv_state, "conv_state", (batch, K - 1, D), K > 1),
         _ptr(h, "h", (batch, D, N)), _ptr(y, "y", (batch, D)), _stream(stream)))
     return y
+
+
+def workspace_bytes(op, *, batch, seq_len, d_inner, d_state, d_conv=1) -> int:
+    """Workspace bytes a backward entry point needs (``op``: OP_* constant)."""
+    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv)
+    n = ctypes.c_size_t(0)
+    _check("mss_workspace_bytes", lib().mss_workspace_bytes(ctypes.byref(dims), op,
+                                                             ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(op, like, workspace, stream, **dims):
+    """The caller's workspace (a uint8 GPU tensor), or a fresh one of the size
+    the library asks for; returns (pointer, bytes, tensor)."""
+    need = workspace_bytes(op, **dims)
+    if workspace is None:
+        if need == 0:
+            return None, 0, None
+        # 256 bytes of slack so that the pointer can be aligned to 256.
+        workspace = _torch().empty(need + 256, dtype=_torch().uint8, device=like.device)
+        if stream is not None:
+            # freed when the caller drops the result: keep it alive for the
+            # work queued on that stream
+            workspace.record_stream(stream)
+    if workspace.dtype != _torch().uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    base = workspace.data_ptr()
+    pad = (-base) % 256
+    return base + pad, max(0, workspace.numel() - pad), workspace
+
+
+def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch, seq_len, disc,
+                            need_dh0=False, workspace=None, stream=None):
+    """Gradients of ``selective_scan``'s output against ``dout`` (batch*seq_len, D).
+
+    Returns a dict: du, ddelta (M, D); dA_log (D, N); dB, dC (M, N);
+    dD (D,) or None when D_vec is None; dz (M, D) or None when z is None;
+    dh0 (batch, D, N) when ``need_dh0``.  ``workspace``: optional uint8 GPU
+    tensor of at least ``workspace_bytes(OP_SELECTIVE_SCAN_BACKWARD, ...)``
+    + 256 bytes (allocated here when omitted).
+    """
+    D, N = A_log.shape
+    M = batch * seq_len
+    g = {"du": _empty((M, D), u), "ddelta": _empty((M, D), u), "dA_log": _empty((D, N), u),
+         "dB": _empty((M, N), u), "dC": _empty((M, N), u),
+         "dD": _empty((D,), u) if D_vec is not None else None,
+         "dz": _empty((M, D), u) if z is not None else None,
+         "dh0": _empty((batch, D, N), u) if need_dh0 else None}
+    wp, wn, _keep = _workspace(OP_SELECTIVE_SCAN_BACKWARD, u, workspace, stream, batch=batch,
+                               seq_len=seq_len, d_inner=D, d_state=N)
+    dims = make_dims(batch, seq_len, D, N)
+    _check("mss_selective_scan_backward", lib().mss_selective_scan_backward(
+        ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
+        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
+        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
+        _ptr(h0, "h0", (batch, D, N), False), _ptr(dout, "dout", (M, D)),
+        _ptr(g["du"], "du", (M, D)), _ptr(g["ddelta"], "ddelta", (M, D)),
+        _ptr(g["dA_log"], "dA_log", (D, N)), _ptr(g["dB"], "dB", (M, N)),
+        _ptr(g["dC"], "dC", (M, N)), _ptr(g["dD"], "dD", (D,), False),
+        _ptr(g["dz"], "dz", (M, D), False), _ptr(g["dh0"], "dh0", (batch, D, N), False),
+        wp, wn, _stream(stream)))
+    return g
+
+
+def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, workspace=None, stream=None):
+    """Gradients of ``conv1d_silu`` against ``du``: (dx, dw_conv, db_conv)."""
+    D, K = w_conv.shape
+    M = batch * seq_len
+    dx, dw, db = _empty((M, D), x), _empty((D, K), x), _empty((D,), x)
+    wp, wn, _keep = _workspace(OP_CONV1D_SILU_BACKWARD, x, workspace, stream, batch=batch,
+                               seq_len=seq_len, d_inner=D, d_state=1, d_conv=K)
+    dims = make_dims(batch, seq_len, D, 1, K)
+    _check("mss_conv1d_silu_backward", lib().mss_conv1d_silu_backward(
+        ctypes.byref(dims), _ptr(x, "x", (M, D)), _ptr(w_conv, "w_conv", (D, K)),
+        _ptr(b_conv, "b_conv", (D,), False), _ptr(du, "du", (M, D)), _ptr(dx, "dx", (M, D)),
+        _ptr(dw, "dw_conv", (D, K)), _ptr(db, "db_conv", (D,)), wp, wn, _stream(stream)))
+    return dx, dw, db

@@ -1,0 +1,129 @@
+// conv_bwd_kernel.hip -- backward of the causal depthwise conv1d + SiLU
+// (mamba1CpuBackward, "SiLU" and "Depthwise causal conv1d" parts,
+// builderforce-memory-engine 2026.7.12 -> 2026.9.27,
+// src/training/mamba1_cpu.ts).  With c the conv output and
+// dc = du * SiLU'(c):
+//   dx[b,t,d] = sum_{k<K, t+k<L} dc[b,t+k,d] * wConv[d,k]
+//   dwConv[d,k] = sum_{b,t>=k} dc[b,t,d] * x[b,t-k,d]
+//   dbConv[d]   = sum_{b,t} dc[b,t,d]
+//
+// HBM-bound (x and du in, dx out: 12 bytes per element).  Lane = channel d;
+// a wave walks 32-step runs with every load of a run issued before first
+// use, recomputing c from x (and dc over the K-1 steps past the run that dx
+// needs).  The dw / db sums stay in registers across all runs of the wave
+// and are written once per wave; a second kernel adds the waves of a channel
+// tile in a fixed order.
+#include "device_math.h"
+#include "launch.h"
+
+namespace mss {
+namespace {
+
+constexpr int kRun = 32;
+constexpr int kPartRows = kMaxK + 1;
+
+__device__ __forceinline__ float silu_grad(float v) {
+    const float s = rcp(1.0f + ex2(-kLog2e * v));
+    return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
+    constexpr int KR = KS > 0 ? KS : kMaxK;
+    const int K = KS > 0 ? KS : a.K;
+    const int64_t L = a.L, D = a.D;
+    const int64_t runs = (L + kRun - 1) / kRun;
+    const int64_t tile = blockIdx.x / a.groups;
+    const int64_t g = blockIdx.x - tile * a.groups;
+    const int64_t d_raw = tile * kWave + threadIdx.x;
+    const bool live = d_raw < D;
+    const int64_t d = live ? d_raw : D - 1;
+
+    float w[KR];
+#pragma unroll
+    for (int k = 0; k < KR; k++) w[k] = k < K ? a.w_conv[d * K + k] : 0.0f;
+    const float bias = a.b_conv ? a.b_conv[d] : 0.0f;
+    float sw[KR], sb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KR; k++) sw[k] = 0.0f;
+
+    constexpr int NX = kRun + 2 * (KR - 1);   // x at t0-(KR-1) .. t0+kRun+KR-2
+    constexpr int NC = kRun + KR - 1;         // dc at t0 .. t0+kRun+KR-2
+    for (int64_t job = g; job < a.B * runs; job += a.groups) {
+        const int64_t b = job / runs;
+        const int64_t t0 = (job - b * runs) * kRun;
+        const int64_t base = b * L * D + d;
+        float xv[NX], gv[NC];
+#pragma unroll
+        for (int i = 0; i < NX; i++) {
+            const int64_t t = t0 - (KR - 1) + i;
+            const int64_t tc = t < 0 ? 0 : (t < L ? t : L - 1);
+            const float v = a.x[base + tc * D];
+            xv[i] = t >= 0 ? v : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+            const int64_t t = t0 + i;
+            const float v = a.du[base + (t < L ? t : L - 1) * D];
+            gv[i] = t < L ? v : 0.0f;
+        }
+        float dc[NC];
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+            float c = bias;
+#pragma unroll
+            for (int k = 0; k < KR; k++) c = __builtin_fmaf(w[k], xv[i + KR - 1 - k], c);
+            dc[i] = gv[i] * silu_grad(c);   // 0 past the sequence end
+        }
+#pragma unroll
+        for (int i = 0; i < kRun; i++) {
+            const int64_t t = t0 + i;
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], dc[i + k], acc);
+            if (live && t < L) a.dx[base + t * D] = acc;
+            // dc[i] is 0 for t >= L, so these sums need no guard.
+            sb += dc[i];
+#pragma unroll
+            for (int k = 0; k < KR; k++) sw[k] = __builtin_fmaf(dc[i], xv[i + KR - 1 - k], sw[k]);
+        }
+    }
+    float* p = a.part + blockIdx.x * static_cast<int64_t>(kPartRows * kWave) + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < KR; k++) p[k * kWave] = sw[k];
+    p[K * kWave] = sb;
+}
+
+__global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(ConvBwdArgs a) {
+    const int64_t d = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    if (d >= a.D) return;
+    const int64_t tile = d / kWave, lane = d - tile * kWave;
+    for (int k = 0; k <= a.K; k++) {
+        if (k == a.K && !a.db) break;
+        float acc = 0.0f;
+        for (int64_t g = 0; g < a.groups; g++)
+            acc += a.part[((tile * a.groups + g) * kPartRows + k) * kWave + lane];
+        if (k < a.K)
+            a.dw[d * a.K + k] = acc;
+        else
+            a.db[d] = acc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_silu_bwd(const ConvBwdArgs& a, hipStream_t st) {
+    const int64_t tiles = (a.D + kWave - 1) / kWave;
+    const unsigned grid = static_cast<unsigned>(tiles * a.groups);
+    if (a.K == 4)
+        hipLaunchKernelGGL(conv_bwd_kernel<4>, dim3(grid), dim3(kWave), 0, st, a);
+    else
+        hipLaunchKernelGGL(conv_bwd_kernel<0>, dim3(grid), dim3(kWave), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3(static_cast<unsigned>((a.D + 255) / 256)),
+                       dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace mss

@@ -239,9 +239,221 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
+constexpr int64_t kBwdTile = 32;     // channels per wave in the scan backward
+constexpr int64_t kBwdBlock = 8;     // steps per checkpointed block
+constexpr int64_t kConvRun = 32;     // steps per job of the conv backward
+constexpr int64_t kConvPartRows = 9; // kMaxK + 1
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Work split of the scan backward: enough segments per (batch row, channel
+// tile) to give about two waves per SIMD, but no segment shorter than
+// MSS_BWD_MIN_SEG steps (default 256), so that the two decay replays of a
+// segment stay a small fraction of its work.
+mss::BwdShape bwd_shape(const mss_dims* dims) {
+    static const int64_t waves_per_cu = env_or("MSS_BWD_WAVES_PER_CU", 8);
+    static const int64_t min_seg = env_or("MSS_BWD_MIN_SEG", 256);
+    mss::BwdShape s;
+    s.B = dims->batch;
+    s.L = dims->seq_len;
+    s.D = dims->d_inner;
+    s.N = static_cast<int>(dims->d_state);
+    s.tiles_per_b = (s.D + kBwdTile - 1) / kBwdTile;
+    const int64_t tiles = s.B * s.tiles_per_b;
+    const int64_t target = cu_count() * waves_per_cu;
+    int64_t nseg = tiles > 0 ? target / tiles : 1;
+    const int64_t max_seg = (s.L + min_seg - 1) / min_seg;
+    if (nseg > max_seg) nseg = max_seg;
+    if (nseg < 1) nseg = 1;
+    s.seg = align_up((s.L + nseg - 1) / (nseg > 0 ? nseg : 1), kBwdBlock);
+    if (s.seg < kBwdBlock) s.seg = kBwdBlock;
+    s.nseg = (s.L + s.seg - 1) / s.seg;
+    if (s.nseg < 1) s.nseg = 1;
+    s.blocks_per_seg = s.seg / kBwdBlock;
+    s.bc_vec = false;
+    return s;
+}
+
+// Byte offsets of the workspace regions of the scan backward.
+struct BwdLayout {
+    int64_t ckpt, partB, partC, partA, partD, total;
+};
+
+bool bwd_layout(const mss::BwdShape& s, BwdLayout& o) {
+    const int64_t waves = s.B * s.tiles_per_b * s.nseg;
+    int64_t ck, pb, pa, pd;
+    if (!count(ck, {waves, s.blocks_per_seg, 64 * 8 * 4}) ||
+        !count(pb, {s.B, s.tiles_per_b, s.L, 16 * 4}) || !count(pa, {waves, 64 * 8 * 4}) ||
+        !count(pd, {waves, 32 * 4}))
+        return false;
+    o.ckpt = 0;
+    o.partB = align_up(o.ckpt + ck, 256);
+    o.partC = align_up(o.partB + pb, 256);
+    o.partA = align_up(o.partC + pb, 256);
+    o.partD = align_up(o.partA + pa, 256);
+    o.total = align_up(o.partD + pd, 256);
+    return true;
+}
+
+int64_t conv_bwd_groups(const mss_dims* dims) {
+    const int64_t tiles = (dims->d_inner + 63) / 64;
+    const int64_t jobs = dims->batch * ((dims->seq_len + kConvRun - 1) / kConvRun);
+    const int64_t target = cu_count() * 8;
+    int64_t g = tiles > 0 ? (target + tiles - 1) / tiles : 1;
+    if (g > jobs) g = jobs;
+    if (g < 1) g = 1;
+    return g;
+}
+
+int64_t conv_bwd_bytes(const mss_dims* dims) {
+    const int64_t tiles = (dims->d_inner + 63) / 64;
+    return align_up(tiles * conv_bwd_groups(dims) * kConvPartRows * 64 * 4, 256);
+}
+
+int check_workspace(void* ws, size_t bytes, int64_t need) {
+    if (need == 0) return MSS_OK;
+    if (!ws || static_cast<int64_t>(bytes) < need) return MSS_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MSS_EALIGN;
+    return MSS_OK;
+}
+
+int zero_fill(float* p, int64_t n, hipStream_t stream) {
+    if (!p || n <= 0) return MSS_OK;
+    const hipError_t e = mss::launch_state_init(nullptr, p, n, stream);
+    return e == hipSuccess ? MSS_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
+
+int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes) {
+    if (!bytes) return MSS_EINVAL;
+    *bytes = 0;
+    if (op == MSS_OP_SELECTIVE_SCAN_BACKWARD) {
+        int st = check_dims(dims, true, false);
+        if (st != MSS_OK) return st;
+        int64_t MD;
+        if (!count(MD, {dims->batch, dims->seq_len, dims->d_inner})) return MSS_EINVAL;
+        if (MD == 0) return MSS_OK;
+        BwdLayout lay;
+        if (!bwd_layout(bwd_shape(dims), lay)) return MSS_EINVAL;
+        *bytes = static_cast<size_t>(lay.total);
+        return MSS_OK;
+    }
+    if (op == MSS_OP_CONV1D_SILU_BACKWARD) {
+        int st = check_dims(dims, true, true);
+        if (st != MSS_OK) return st;
+        int64_t MD;
+        if (!count(MD, {dims->batch, dims->seq_len, dims->d_inner})) return MSS_EINVAL;
+        if (MD == 0) return MSS_OK;
+        *bytes = static_cast<size_t>(conv_bwd_bytes(dims));
+        return MSS_OK;
+    }
+    return MSS_EINVAL;
+}
+
+int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
+                                const float* delta, const float* A_log, const float* B,
+                                const float* C, const float* D_vec, const float* z,
+                                const float* h0, const float* dout, float* du, float* ddelta,
+                                float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
+                                float* dh0, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    int st = check_dims(dims, true, false);
+    if (st != MSS_OK) return st;
+    if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
+    const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
+    int64_t MD, MN, DN, BDN;
+    if (!count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) || !count(DN, {D, N}) ||
+        !count(BDN, {Bt, D, N}))
+        return MSS_EINVAL;
+    if (z && !dz && MD > 0) return MSS_EINVAL;
+    Checker ck;
+    ck.in(u, MD, true);
+    ck.in(delta, MD, true);
+    ck.in(A_log, DN, true);
+    ck.in(B, MN, true);
+    ck.in(C, MN, true);
+    ck.in(D_vec, D, false);
+    ck.in(z, MD, false);
+    ck.in(h0, BDN, false);
+    ck.in(dout, MD, true);
+    ck.out(du, MD, true);
+    ck.out(ddelta, MD, true);
+    ck.out(dA_log, DN, true);
+    ck.out(dB, MN, true);
+    ck.out(dC, MN, true);
+    ck.out(dD_vec, D, false);
+    ck.out(dz, z ? MD : 0, false);
+    ck.out(dh0, BDN, false);
+    int64_t need = 0;
+    mss::BwdShape s{};
+    BwdLayout lay{};
+    if (MD > 0) {
+        s = bwd_shape(dims);
+        if (!bwd_layout(s, lay)) return MSS_EINVAL;
+        need = lay.total;
+    }
+    // The workspace is an output like the others: it may not overlap anything.
+    if (need > 0 && workspace) ck.outs.push_back({workspace, need});
+    st = ck.finish();
+    if (st != MSS_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != MSS_OK) return st;
+    if (MD == 0) {
+        // Nothing depends on the parameters: their gradients are zero.
+        if ((st = zero_fill(dA_log, DN, stream)) != MSS_OK) return st;
+        if ((st = zero_fill(dD_vec, D, stream)) != MSS_OK) return st;
+        return zero_fill(dh0, BDN, stream);
+    }
+    s.bc_vec = N == 16 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
+               reinterpret_cast<uintptr_t>(C) % 16 == 0;
+    char* w = static_cast<char*>(workspace);
+    const mss::BwdArgs a{disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta, dA_log,
+                         dB, dC, dD_vec, z ? dz : nullptr, dh0,
+                         reinterpret_cast<float*>(w + lay.ckpt),
+                         reinterpret_cast<float*>(w + lay.partB),
+                         reinterpret_cast<float*>(w + lay.partC),
+                         reinterpret_cast<float*>(w + lay.partA),
+                         reinterpret_cast<float*>(w + lay.partD)};
+    const hipError_t e = mss::launch_scan_bwd(a, s, stream);
+    return e == hipSuccess ? MSS_OK : hip_fail(e);
+}
+
+int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* w_conv,
+                             const float* b_conv, const float* du, float* dx, float* dw_conv,
+                             float* db_conv, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    int st = check_dims(dims, true, true);
+    if (st != MSS_OK) return st;
+    const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, K = dims->d_conv;
+    int64_t MD;
+    if (!count(MD, {Bt, L, D})) return MSS_EINVAL;
+    Checker ck;
+    ck.in(x, MD, true);
+    ck.in(w_conv, D * K, true);
+    ck.in(b_conv, D, false);
+    ck.in(du, MD, true);
+    ck.out(dx, MD, true);
+    ck.out(dw_conv, D * K, true);
+    ck.out(db_conv, D, false);
+    const int64_t need = MD > 0 ? conv_bwd_bytes(dims) : 0;
+    if (need > 0 && workspace) ck.outs.push_back({workspace, need});
+    st = ck.finish();
+    if (st != MSS_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != MSS_OK) return st;
+    if (MD == 0) {
+        if ((st = zero_fill(dw_conv, D * K, stream)) != MSS_OK) return st;
+        return zero_fill(db_conv, D, stream);
+    }
+    const mss::ConvBwdArgs a{Bt, L, D, static_cast<int>(K), conv_bwd_groups(dims), x, w_conv,
+                             b_conv, du, dx, dw_conv, db_conv, static_cast<float*>(workspace)};
+    const hipError_t e = mss::launch_conv1d_silu_bwd(a, stream);
+    return e == hipSuccess ? MSS_OK : hip_fail(e);
+}
+
 
 int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv, const float* b_conv,
                     float* u, hipStream_t stream) {
@@ -338,6 +550,7 @@ const char* mss_strerror(int status) {
         case MSS_EINVAL: return "invalid argument (null tensor, size out of range, bad struct_size or disc)";
         case MSS_EALIGN: return "pointer not 16-byte aligned";
         case MSS_EALIAS: return "an output overlaps an input or another output";
+        case MSS_EWORKSPACE: return "workspace missing or smaller than mss_workspace_bytes reports";
         case MSS_EHIP: return "HIP runtime error (see mss_last_hip_error)";
         default: return "unknown status";
     }

@@ -1,0 +1,675 @@
+// scan_bwd_kernel.hip -- backward pass of the selective scan and its gate for
+// gfx950.
+//
+// Computes the reverse-time adjoint of mamba1CpuBackward (builderforce-memory-
+// engine 2026.7.12 -> 2026.9.27, src/training/mamba1_cpu.ts: the gate, the
+// scan "walked backwards in time", the A_log clamp mask and softplus): per
+// (b, d) column, with dY = dout SiLU(z), g_n the adjoint carried from step
+// t+1 and dh_n = C_n dY + g_n,
+//   du = D dY + sum_n dh_n bBar_n            g_n <- dh_n aBar_n
+//   ddv = sum_n aBar_n (dh_n h_{t-1,n} A_n + dh_n u dbBar_n/ddv / aBar_n)
+//   dA_n += dv aBar_n dh_n h_{t-1,n} + dh_n u dbBar_n/dA
+//   dB[r,n] = sum_d dh_n u dbBar_n/dB          dC[r,n] = sum_d dY h_t,n
+//   dz = dout y SiLU'(z),  ddelta = ddv sigmoid(delta),  dD = sum dY u
+//
+// Mapping.  One wave64 per (batch row, 32 channels, time segment); lane
+// (half, q) owns channel q of the tile and the 8 states n = 8 half + j, so
+// the per-lane state vectors (h, adjoint, dA) stay at 8 registers each and
+// the two halves of a channel combine their sums with one cross-half add.
+//
+// Work per segment [t0, t1):
+//   1. h(t0-1) by decay-bounded forward replay (as in the forward kernel).
+//   2. Forward over the segment, storing h at every 8-step block start in the
+//      checkpoint workspace (2 KB per block).
+//   3. The adjoint carried into t1-1 by decay-bounded reverse replay: walk
+//      delta forward from t1 until every lane's slowest state has decayed by
+//      2^-30, then run the adjoint recurrence backwards from there with g = 0.
+//   4. Blocks in reverse order: reload the block's checkpoint, recompute its
+//      8 states into registers (emitting dz and the dC terms on the way),
+//      then run the adjoint through the block (emitting du, ddelta and the dB
+//      terms).
+// Cross-channel sums: each step's 8 dB (or dC) values per lane are reduced
+// over the 32 channels of the tile with a transpose-reduce (one exchange
+// level per lane bit, DPP and ds_swizzle), then written per tile to a
+// partial buffer that a second kernel sums over tiles in a fixed order; dA
+// and dD are written per wave and summed the same way.  No atomics: the
+// result is bitwise reproducible.
+#include "device_math.h"
+#include "launch.h"
+
+namespace mss {
+namespace {
+
+constexpr int kT = 8;                          // steps per block
+constexpr int kH = 8;                          // states per lane
+constexpr int kBackBlk = 16;
+constexpr float kDecayCut = 30.0f;
+constexpr float kSmallX = 0.015625f;           // expm1 cubic below |dv A| = 2^-6
+constexpr float kSmallX2 = kSmallX * kLog2e;
+constexpr float kPhiX = 0.125f;                // ZOH dA series below |dv A| = 1/8
+constexpr float kPhiX2 = kPhiX * kLog2e;
+
+struct BwdCols {
+    const float* __restrict__ u;
+    const float* __restrict__ delta;
+    const float* __restrict__ A_log;
+    const float* __restrict__ Bm;
+    const float* __restrict__ Cm;
+    const float* __restrict__ Dv;
+    const float* __restrict__ z;
+    const float* __restrict__ h0;
+    const float* __restrict__ dout;
+    float* __restrict__ du;
+    float* __restrict__ ddelta;
+    float* __restrict__ dz;
+    float* __restrict__ dh0;
+    float* __restrict__ ckpt;     // (waves, blocks per segment, 64, 8)
+    float* __restrict__ partB;    // (B, tiles, L, 16)
+    float* __restrict__ partC;    // (B, tiles, L, 16)
+    float* __restrict__ partA;    // (waves, 64, 8)
+    float* __restrict__ partD;    // (waves, 32)
+};
+
+__device__ __forceinline__ float as_f(int v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ int as_i(float v) { return __builtin_bit_cast(int, v); }
+
+// Lane exchanges inside a 32-lane half.
+__device__ __forceinline__ float xor16(float v) {   // ds_swizzle, bit mode: and 0x1f, xor 0x10
+    return as_f(__builtin_amdgcn_ds_swizzle(as_i(v), 0x401f));
+}
+__device__ __forceinline__ float xor8(float v) {    // DPP row_ror:8 (rotation by 8 in 16 lanes)
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0x128, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xor7(float v) {    // DPP row_half_mirror (lane i <-> 7 - i)
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0x141, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xor2(float v) {    // DPP quad_perm [2,3,0,1]
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0x4e, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xor1(float v) {    // DPP quad_perm [1,0,3,2]
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0xb1, 0xf, 0xf, true));
+}
+// Sum of the two halves of a channel (lanes l and l ^ 32).
+__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32); }
+
+// Sum over the 32 lanes of this half of v[j], for j = q >> 2 (q = lane & 31):
+// three exchange levels that each keep half of the values (selected by lane
+// bits 4, 3, 2) and add the partner's other half, then two plain levels.
+__device__ __forceinline__ float reduce8(const float (&v)[kH]) {
+    const uint32_t q = threadIdx.x & 31u;
+    const bool b4 = q & 16u, b3 = q & 8u, b2 = q & 4u;
+    float w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float keep = b4 ? v[i + 4] : v[i];
+        const float send = b4 ? v[i] : v[i + 4];
+        w4[i] = keep + xor16(send);
+    }
+    float w2[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const float keep = b3 ? w4[i + 2] : w4[i];
+        const float send = b3 ? w4[i] : w4[i + 2];
+        w2[i] = keep + xor8(send);
+    }
+    const float keep = b2 ? w2[1] : w2[0];
+    const float send = b2 ? w2[0] : w2[1];
+    float w1 = keep + xor7(send);
+    w1 += xor2(w1);
+    w1 += xor1(w1);
+    return w1;
+}
+
+// d SiLU / dv = s (1 + v (1 - s)), s = sigmoid(v).
+__device__ __forceinline__ float silu_grad(float v) {
+    const float s = rcp(1.0f + ex2(-kLog2e * v));
+    return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
+}
+__device__ __forceinline__ float sigmoid(float v) { return rcp(1.0f + ex2(-kLog2e * v)); }
+
+// expm1(x) for |x| < 2^-6 (relative truncation < 2e-7) else a - 1.
+__device__ __forceinline__ float em1_of(float x, float a) {
+    const float p = x * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 6.0f, 0.5f), 1.0f);
+    return __builtin_fabsf(x) < kSmallX ? p : a - 1.0f;
+}
+
+template <int DISC, int NS>
+struct Bwd {
+    static constexpr bool kZoh = DISC == MSS_DISC_ZOH;
+
+    const BwdCols& c;
+    const int64_t L, D;
+    const int N;
+    const int64_t b;
+    const uint32_t d;          // channel, clamped to D - 1
+    const bool live;           // the lane's channel exists
+    const uint32_t half;
+    const bool gated;
+    float4* lds;               // 8 steps: B rows [0, 32), C rows [32, 64) (16 floats per row)
+
+    float A2[kH], Ai[kH], An[kH];
+    float min_a2, dvec;
+
+    __device__ Bwd(const BwdCols& c_, const BwdShape& s, int64_t b_, int64_t d_raw, float4* lds_)
+        : c(c_), L(s.L), D(s.D), N(NS > 0 ? NS : s.N), b(b_),
+          d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)), live(d_raw < s.D),
+          half(threadIdx.x >> 5), gated(c_.z != nullptr), lds(lds_) {}
+
+    __device__ __forceinline__ bool valid(int j) const {
+        return NS > 0 || static_cast<int>(half) * kH + j < N;
+    }
+    __device__ __forceinline__ int64_t row(int64_t t) const { return b * L + t; }
+    __device__ __forceinline__ float ld(const float* base, int64_t t) const {
+        return base[row(t) * D + d];
+    }
+
+    __device__ __forceinline__ void init() {
+        float mn = 3.0e38f;
+#pragma unroll
+        for (int j = 0; j < kH; j++) {
+            if (valid(j)) {
+                const float A = a_cont(c.A_log[d * N + half * kH + j]);
+                An[j] = A;
+                A2[j] = A * kLog2e;
+                Ai[j] = 1.0f / A;
+                mn = __builtin_fminf(mn, -A2[j]);
+            } else {
+                An[j] = -1.0f;
+                A2[j] = -kLog2e;
+                Ai[j] = -1.0f;
+            }
+        }
+        min_a2 = mn;
+        dvec = c.Dv ? c.Dv[d] : 0.0f;
+    }
+
+    // B and C rows of steps t0 .. t0+7 into LDS, zero-padded to 16 states
+    // (rows past the sequence end repeat its last row and are never used).
+    __device__ __forceinline__ void stage(int64_t t0) const {
+        const uint32_t lane = threadIdx.x;
+        const uint32_t q = lane & 31u;
+        int64_t t = t0 + (q >> 2);
+        t = t < L ? t : L - 1;
+        const float* base = (lane < 32 ? c.Bm : c.Cm) + row(t) * N;
+        const int col = static_cast<int>(q & 3u) * 4;
+        float4 v;
+        if constexpr (NS == 16) {
+            v = *reinterpret_cast<const float4*>(base + col);
+        } else {
+            v.x = col + 0 < N ? base[col + 0] : 0.0f;
+            v.y = col + 1 < N ? base[col + 1] : 0.0f;
+            v.z = col + 2 < N ? base[col + 2] : 0.0f;
+            v.w = col + 3 < N ? base[col + 3] : 0.0f;
+        }
+        __builtin_amdgcn_wave_barrier();
+        lds[lane] = v;
+        __builtin_amdgcn_wave_barrier();
+    }
+    __device__ __forceinline__ void read_row(int base, int i, float (&v)[kH]) const {
+        const float4 p = lds[base + i * 4 + 2 * half];
+        const float4 q = lds[base + i * 4 + 2 * half + 1];
+        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    }
+
+    // ---- forward state update (as the forward kernel) -------------------
+    template <bool SLOW>
+    __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv, const float (&Bv)[kH]) const {
+        const float dvu = dv * uv;
+#pragma unroll
+        for (int j = 0; j < kH; j++) {
+            if (!valid(j)) continue;
+            const float x2 = dv * A2[j];
+            const float a = ex2(x2);
+            if constexpr (!SLOW) {
+                if constexpr (kZoh) {
+                    const float k = (uv * Ai[j]) * Bv[j];
+                    h[j] = __builtin_fmaf(a, h[j] + k, -k);
+                } else {
+                    h[j] = __builtin_fmaf(a, h[j], dvu * Bv[j]);
+                }
+            } else {
+                const float m = em1_of(x2 * kLn2, a);
+                if constexpr (kZoh) {
+                    const float k = (uv * Ai[j]) * Bv[j];
+                    h[j] = __builtin_fmaf(m, h[j] + k, h[j]);
+                } else {
+                    h[j] = __builtin_fmaf(dvu, Bv[j], __builtin_fmaf(m, h[j], h[j]));
+                }
+            }
+        }
+    }
+
+    // ---- reverse (adjoint) step ------------------------------------------
+    // FULL: also the gradients (du, ddv, dA, dB terms); otherwise only g.
+    template <bool SLOW, bool FULL>
+    __device__ __forceinline__ void rev(float (&g)[kH], float (&dA)[kH], const float (&hp)[kH],
+                                        float uv, float dv, float dY, const float (&Bv)[kH],
+                                        const float (&Cv)[kH], float& du_acc, float& ddv_acc,
+                                        float (&dBp)[kH]) const {
+#pragma unroll
+        for (int j = 0; j < kH; j++) {
+            if (!valid(j)) {
+                if constexpr (FULL) dBp[j] = 0.0f;
+                continue;
+            }
+            const float x2 = dv * A2[j];
+            const float a = ex2(x2);
+            const float dh = __builtin_fmaf(Cv[j], dY, g[j]);
+            float m = 0.0f;
+            if constexpr (SLOW) {
+                m = em1_of(x2 * kLn2, a);
+                g[j] = __builtin_fmaf(m, dh, dh);
+            } else {
+                g[j] = dh * a;
+            }
+            if constexpr (FULL) {
+                const float dab = dh * hp[j];
+                const float dbb = dh * uv;
+                if constexpr (kZoh) {
+                    if constexpr (!SLOW) m = a - 1.0f;
+                    const float q = m * Ai[j];                     // (aBar - 1) / A
+                    du_acc = __builtin_fmaf(dh, q * Bv[j], du_acc);
+                    dBp[j] = dbb * q;
+                    const float wv = dbb * Bv[j];
+                    ddv_acc = __builtin_fmaf(a, __builtin_fmaf(dab, An[j], wv), ddv_acc);
+                    // (dv aBar A - (aBar - 1)) / A^2 = Ai (dv aBar - q); below
+                    // |dv A| = 1/8 that difference cancels and is taken from
+                    // its series dv x (1/2 + x/3 + x^2/8 + x^3/30), x = dv A.
+                    float t5 = __builtin_fmaf(dv, a, -q);
+                    if constexpr (SLOW) {
+                        const float x = x2 * kLn2;
+                        const float ph = __builtin_fmaf(
+                            x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f),
+                            0.5f);
+                        t5 = __builtin_fabsf(x) < kPhiX ? (dv * x) * ph : t5;
+                    }
+                    dA[j] = __builtin_fmaf(dv, a * dab, dA[j]);
+                    dA[j] = __builtin_fmaf(wv * Ai[j], t5, dA[j]);
+                } else {
+                    du_acc = __builtin_fmaf(dh, dv * Bv[j], du_acc);
+                    dBp[j] = dbb * dv;
+                    const float ad = a * dab;
+                    ddv_acc = __builtin_fmaf(ad, An[j], ddv_acc);
+                    ddv_acc = __builtin_fmaf(dbb, Bv[j], ddv_acc);
+                    dA[j] = __builtin_fmaf(dv, ad, dA[j]);
+                }
+            }
+        }
+    }
+
+    // ---- decay-bounded replay bounds --------------------------------------
+    __device__ int64_t replay_start(int64_t t0) const {
+        if (t0 == 0) return 0;
+        float S = 0.0f;
+        int64_t t = t0;
+        while (true) {
+            float dd[kBackBlk];
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t - 1 - i;
+                dd[i] = ld(c.delta, tt >= 0 ? tt : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t - 1 - i;
+                if (tt < 0) return 0;
+                S += softplus(dd[i]);
+                if (wave_all(S * min_a2 >= kDecayCut)) return tt;
+            }
+            t -= kBackBlk;
+        }
+    }
+
+    // End (exclusive) of the reverse replay that carries the adjoint into t1-1.
+    __device__ int64_t replay_end(int64_t t1) const {
+        if (t1 >= L) return L;
+        float S = 0.0f;
+        int64_t t = t1;
+        while (true) {
+            float dd[kBackBlk];
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t + i;
+                dd[i] = ld(c.delta, tt < L ? tt : L - 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kBackBlk; i++) {
+                const int64_t tt = t + i;
+                if (tt >= L) return L;
+                S += softplus(dd[i]);
+                if (wave_all(S * min_a2 >= kDecayCut)) return tt + 1;
+            }
+            t += kBackBlk;
+        }
+    }
+
+    // Block choice.  Forward-type passes: as the forward kernel (every lane's
+    // slowest state decays by at least exp(-8 2^-6) over the block).  Reverse
+    // passes, ZOH: every step of the block has |dv A| >= 1/8 in every state
+    // (the dA term needs no series); EULER: as the forward passes.
+    __device__ __forceinline__ bool slow_fwd(const float (&dv)[kT], int n) const {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kT; i++) s += i < n ? dv[i] : 0.0f;
+        return wave_any(s * min_a2 < n * kSmallX2);
+    }
+    __device__ __forceinline__ bool slow_rev(const float (&dv)[kT], int n) const {
+        if constexpr (!kZoh) return slow_fwd(dv, n);
+        float mn = 3.0e38f;
+#pragma unroll
+        for (int i = 0; i < kT; i++) mn = i < n ? __builtin_fminf(mn, dv[i]) : mn;
+        return wave_any(mn * min_a2 < kPhiX2);
+    }
+
+    // ---- forward sweep over [ta, tb) in blocks of 8 from ta ---------------
+    // CKPT: store h at every block start to ck (2 KB per block, lane-major).
+    template <bool CKPT>
+    __device__ void fwd_sweep(float (&h)[kH], int64_t ta, int64_t tb, float* ck) const {
+        for (int64_t s = ta; s < tb; s += kT) {
+            const int n = tb - s < kT ? static_cast<int>(tb - s) : kT;
+            if constexpr (CKPT) {
+                float4* p = reinterpret_cast<float4*>(ck) + threadIdx.x * 2;
+                p[0] = make_float4(h[0], h[1], h[2], h[3]);
+                p[1] = make_float4(h[4], h[5], h[6], h[7]);
+                ck += kWave * kH;
+            }
+            float uu[kT], dv[kT];
+#pragma unroll
+            for (int i = 0; i < kT; i++) {
+                const int64_t t = s + i < L ? s + i : L - 1;
+                uu[i] = ld(c.u, t);
+                dv[i] = ld(c.delta, t);
+            }
+            stage(s);
+#pragma unroll
+            for (int i = 0; i < kT; i++) dv[i] = softplus(dv[i]);
+            if (!slow_fwd(dv, n)) {
+#pragma unroll
+                for (int i = 0; i < kT; i++) {
+                    if (i >= n) break;
+                    float Bv[kH];
+                    read_row(0, i, Bv);
+                    fwd<false>(h, uu[i], dv[i], Bv);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kT; i++) {
+                    if (i >= n) break;
+                    float Bv[kH];
+                    read_row(0, i, Bv);
+                    fwd<true>(h, uu[i], dv[i], Bv);
+                }
+            }
+        }
+    }
+
+    // dY of step t (0 for lanes without a channel).
+    __device__ __forceinline__ float grad_y(float go, float zv) const {
+        const float v = gated ? go * silu(zv) : go;
+        return live ? v : 0.0f;
+    }
+
+    // ---- reverse replay over [ta, tb), adjoint only -----------------------
+    __device__ void rev_sweep(float (&g)[kH], int64_t ta, int64_t tb) const {
+        const int64_t nb = (tb - ta + kT - 1) / kT;
+        for (int64_t k = nb - 1; k >= 0; k--) {
+            const int64_t s = ta + k * kT;
+            const int n = tb - s < kT ? static_cast<int>(tb - s) : kT;
+            float dv[kT], dY[kT];
+#pragma unroll
+            for (int i = 0; i < kT; i++) {
+                const int64_t t = s + i < L ? s + i : L - 1;
+                dv[i] = ld(c.delta, t);
+                const float go = ld(c.dout, t);
+                const float zv = gated ? ld(c.z, t) : 0.0f;
+                dY[i] = grad_y(go, zv);
+            }
+            stage(s);
+#pragma unroll
+            for (int i = 0; i < kT; i++) dv[i] = softplus(dv[i]);
+            // Only g is updated; the gradient arguments are not read.
+            float dA[kH] = {}, hp[kH] = {}, dBp[kH], Bv[kH] = {}, du_acc = 0.0f, ddv_acc = 0.0f;
+            if (!slow_rev(dv, n)) {
+#pragma unroll
+                for (int i = kT - 1; i >= 0; i--) {
+                    if (i >= n) continue;
+                    float Cv[kH];
+                    read_row(32, i, Cv);
+                    rev<false, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+                }
+            } else {
+#pragma unroll
+                for (int i = kT - 1; i >= 0; i--) {
+                    if (i >= n) continue;
+                    float Cv[kH];
+                    read_row(32, i, Cv);
+                    rev<true, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+                }
+            }
+        }
+    }
+
+    // ---- one block of the main pass ---------------------------------------
+    template <bool SLOW>
+    __device__ __forceinline__ void block(float (&g)[kH], float (&dA)[kH], float& dD,
+                                          const float (&h_in)[kH], int64_t s, int n,
+                                          const float (&uu)[kT], const float (&dl)[kT],
+                                          const float (&dv)[kT], const float (&go)[kT],
+                                          const float (&zz)[kT], float* pB, float* pC) const {
+        float hist[kT][kH];
+        float dY[kT];
+        float h[kH];
+#pragma unroll
+        for (int j = 0; j < kH; j++) h[j] = hist[0][j] = h_in[j];
+        const bool writer = live && half == 0;
+        const bool red_writer = (threadIdx.x & 3u) == 0;
+        const uint32_t n_out = half * kH + ((threadIdx.x & 31u) >> 2);
+        // Recompute the block's states (forward), with dz and the dC terms.
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            if (i >= n) break;
+            float Bv[kH], Cv[kH];
+            read_row(0, i, Bv);
+            read_row(32, i, Cv);
+            fwd<SLOW>(h, uu[i], dv[i], Bv);
+            if (i + 1 < kT) {
+#pragma unroll
+                for (int j = 0; j < kH; j++) hist[i + 1][j] = h[j];
+            }
+            float yp = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kH; j++) yp = __builtin_fmaf(Cv[j], h[j], yp);
+            const float y = __builtin_fmaf(dvec, uu[i], pair_sum(yp));
+            dY[i] = grad_y(go[i], zz[i]);
+            const int64_t r = row(s + i);
+            if (gated && writer) c.dz[r * D + d] = go[i] * y * silu_grad(zz[i]);
+            float dCp[kH];
+#pragma unroll
+            for (int j = 0; j < kH; j++) dCp[j] = dY[i] * h[j];
+            const float sC = reduce8(dCp);
+            if (red_writer) pC[(s + i) * 16 + n_out] = sC;
+        }
+        // Adjoint through the block, newest step first.
+#pragma unroll
+        for (int i = kT - 1; i >= 0; i--) {
+            if (i >= n) continue;
+            float Bv[kH], Cv[kH], dBp[kH];
+            read_row(0, i, Bv);
+            read_row(32, i, Cv);
+            float du_acc = 0.0f, ddv_acc = 0.0f;
+            rev<SLOW, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+            const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
+            const float ddv = pair_sum(ddv_acc);
+            const int64_t r = row(s + i);
+            if (writer) {
+                c.du[r * D + d] = duv;
+                c.ddelta[r * D + d] = ddv * sigmoid(dl[i]);
+            }
+            dD = __builtin_fmaf(dY[i], uu[i], dD);
+            const float sB = reduce8(dBp);
+            if (red_writer) pB[(s + i) * 16 + n_out] = sB;
+        }
+    }
+};
+
+template <int DISC, int NS>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_bwd_kernel(
+    BwdCols c, BwdShape s) {
+    __shared__ float4 lds[kWave];
+    const int64_t w = blockIdx.x;
+    const int64_t ti = w / s.nseg;
+    const int64_t sg = w - ti * s.nseg;
+    const int64_t b = ti / s.tiles_per_b;
+    const int64_t ct = ti - b * s.tiles_per_b;
+    const uint32_t lane = threadIdx.x;
+    const int64_t t0 = sg * s.seg;
+    const int64_t t1 = t0 + s.seg < s.L ? t0 + s.seg : s.L;
+
+    Bwd<DISC, NS> bw(c, s, b, ct * 32 + (lane & 31u), lds);
+    bw.init();
+
+    // 1. h(t0 - 1)
+    float h[kH];
+    const int64_t tw = bw.replay_start(t0);
+#pragma unroll
+    for (int j = 0; j < kH; j++)
+        h[j] = (tw == 0 && c.h0 && bw.valid(j)) ? c.h0[(b * s.D + bw.d) * bw.N + bw.half * kH + j] : 0.0f;
+    bw.template fwd_sweep<false>(h, tw, t0, nullptr);
+
+    // 2. checkpoints of the segment
+    float* ck = c.ckpt + w * s.blocks_per_seg * (kWave * kH);
+    bw.template fwd_sweep<true>(h, t0, t1, ck);
+    // The checkpoints are read back by this wave below.
+    __threadfence_block();
+
+    // 3. adjoint carried into t1 - 1
+    float g[kH];
+#pragma unroll
+    for (int j = 0; j < kH; j++) g[j] = 0.0f;
+    bw.rev_sweep(g, t1, bw.replay_end(t1));
+
+    // 4. blocks of the segment, newest first
+    float dA[kH];
+#pragma unroll
+    for (int j = 0; j < kH; j++) dA[j] = 0.0f;
+    float dD = 0.0f;
+    float* pB = c.partB + ti * s.L * 16;
+    float* pC = c.partC + ti * s.L * 16;
+    const int64_t nb = (t1 - t0 + kT - 1) / kT;
+    for (int64_t k = nb - 1; k >= 0; k--) {
+        const int64_t st = t0 + k * kT;
+        const int n = t1 - st < kT ? static_cast<int>(t1 - st) : kT;
+        float uu[kT], dl[kT], dv[kT], go[kT], zz[kT];
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            const int64_t t = st + i < s.L ? st + i : s.L - 1;
+            uu[i] = bw.ld(c.u, t);
+            dl[i] = bw.ld(c.delta, t);
+            go[i] = bw.ld(c.dout, t);
+            zz[i] = c.z ? bw.ld(c.z, t) : 0.0f;
+        }
+        const float4* p = reinterpret_cast<const float4*>(ck + k * (kWave * kH)) + lane * 2;
+        const float4 h_lo = p[0], h_hi = p[1];
+        const float hin[kH] = {h_lo.x, h_lo.y, h_lo.z, h_lo.w, h_hi.x, h_hi.y, h_hi.z, h_hi.w};
+        bw.stage(st);
+#pragma unroll
+        for (int i = 0; i < kT; i++) dv[i] = softplus(dl[i]);
+        // The reverse criterion implies the forward one (ZOH: every step has
+        // |dv A| >= 1/8; EULER: the two are the same).
+        if (!bw.slow_rev(dv, n))
+            bw.template block<false>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
+        else
+            bw.template block<true>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
+    }
+
+    // 5. per-wave partial sums and dh0
+    float4* pa = reinterpret_cast<float4*>(c.partA + (w * kWave + lane) * kH);
+    pa[0] = make_float4(dA[0], dA[1], dA[2], dA[3]);
+    pa[1] = make_float4(dA[4], dA[5], dA[6], dA[7]);
+    if (lane < 32) c.partD[w * 32 + lane] = dD;
+    if (t0 == 0 && c.dh0 && bw.live) {
+#pragma unroll
+        for (int j = 0; j < kH; j++)
+            if (bw.valid(j)) c.dh0[(b * s.D + bw.d) * bw.N + bw.half * kH + j] = g[j];
+    }
+}
+
+// Cross-tile and cross-segment sums, fixed order:
+//   dB[r, n], dC[r, n] = sum over channel tiles of the partial rows;
+//   dA_log[d, n] = A[d, n] * sum over (b, segment) (0 outside the clamp);
+//   dD[d] = sum over (b, segment).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdCols c, BwdShape s, float* dB,
+                                                         float* dC, float* dA_log, float* dD) {
+    const int64_t M = s.B * s.L;
+    const int64_t nBC = M * s.N;
+    const int64_t nA = s.D * s.N;
+    const int64_t total = nBC + nA + (dD ? s.D : 0);
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        if (i < nBC) {
+            const int64_t r = i / s.N, n = i - r * s.N;
+            const int64_t b = r / s.L, t = r - b * s.L;
+            float sb = 0.0f, sc = 0.0f;
+            for (int64_t ct = 0; ct < s.tiles_per_b; ct++) {
+                const int64_t o = ((b * s.tiles_per_b + ct) * s.L + t) * 16 + n;
+                sb += c.partB[o];
+                sc += c.partC[o];
+            }
+            dB[i] = sb;
+            dC[i] = sc;
+        } else if (i < nBC + nA) {
+            const int64_t e = i - nBC;
+            const int64_t d = e / s.N, n = e - d * s.N;
+            const int64_t ct = d / 32, q = d - ct * 32;
+            const int64_t lane = (n / kH) * 32 + q, j = n % kH;
+            float acc = 0.0f;
+            for (int64_t b = 0; b < s.B; b++)
+                for (int64_t sg = 0; sg < s.nseg; sg++) {
+                    const int64_t w = (b * s.tiles_per_b + ct) * s.nseg + sg;
+                    acc += c.partA[(w * kWave + lane) * kH + j];
+                }
+            const float al = c.A_log[e];
+            dA_log[e] = (al <= -10.0f || al >= 5.0f) ? 0.0f : acc * a_cont(al);
+        } else {
+            const int64_t d = i - nBC - nA;
+            const int64_t ct = d / 32, q = d - ct * 32;
+            float acc = 0.0f;
+            for (int64_t b = 0; b < s.B; b++)
+                for (int64_t sg = 0; sg < s.nseg; sg++)
+                    acc += c.partD[((b * s.tiles_per_b + ct) * s.nseg + sg) * 32 + q];
+            dD[d] = acc;
+        }
+    }
+}
+
+template <int DISC, int NS>
+hipError_t launch_t(const BwdCols& c, const BwdShape& s, hipStream_t st) {
+    const int64_t nw = s.B * s.tiles_per_b * s.nseg;
+    hipLaunchKernelGGL((scan_bwd_kernel<DISC, NS>), dim3(static_cast<unsigned>(nw)), dim3(kWave),
+                       0, st, c, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs& a, const BwdShape& s, hipStream_t st) {
+    BwdCols c{a.u,  a.delta,  a.A_log, a.B,    a.C,     a.D_vec, a.z,     a.h0,    a.dout,
+              a.du, a.ddelta, a.dz,    a.dh0,  a.ckpt,  a.partB, a.partC, a.partA, a.partD};
+    hipError_t e;
+    const bool vec = s.N == 16 && s.bc_vec;
+    if (a.disc == MSS_DISC_EULER)
+        e = vec ? launch_t<MSS_DISC_EULER, 16>(c, s, st) : launch_t<MSS_DISC_EULER, 0>(c, s, st);
+    else
+        e = vec ? launch_t<MSS_DISC_ZOH, 16>(c, s, st) : launch_t<MSS_DISC_ZOH, 0>(c, s, st);
+    if (e != hipSuccess) return e;
+    const int64_t total = s.B * s.L * s.N + s.D * s.N + (a.dD_vec ? s.D : 0);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, c,
+                       s, a.dB, a.dC, a.dA_log, a.dD_vec);
+    return hipGetLastError();
+}
+
+}  // namespace mss

@@ -164,3 +164,10 @@ def generate(w: Workload, seed_offset: int = 0, threads: int = 8) -> dict:
     elif w.h0:
         out["h0"] = _normal(ch["h0"], (w.batch, D, N), 0.0, w.h_var, threads)
     return out
+
+
+def cotangent(w: Workload, seed_offset: int = 0, threads: int = 8) -> np.ndarray:
+    """A seeded N(0, 1) gradient of the output (M, D) for the backward passes,
+    from a stream of its own (the inputs of ``generate`` are unchanged)."""
+    seq = np.random.SeedSequence([SEED_BASE + w.seed_index + 1000 * seed_offset, 0xD07])
+    return _normal(seq, (w.M, w.d_inner), 0.0, 1.0, threads)

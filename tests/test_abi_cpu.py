@@ -39,7 +39,8 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_strerror(L):
     assert L.mss_version() == header_define("MSS_VERSION")
-    for name in ("MSS_OK", "MSS_EINVAL", "MSS_EALIGN", "MSS_EALIAS", "MSS_EHIP"):
+    for name in ("MSS_OK", "MSS_EINVAL", "MSS_EALIGN", "MSS_EALIAS", "MSS_EWORKSPACE",
+                 "MSS_EHIP"):
         s = L.mss_strerror(header_define(name))
         assert s and s != b"unknown status"
     assert L.mss_strerror(12345) == b"unknown status"
@@ -193,3 +194,81 @@ def test_strided_validation(L):
     assert L.mss_selective_scan_strided(ctypes.byref(d0), ctypes.byref(ok), 1, None, None, None,
                                         fake(5), fake(6), None, None, None, None, None, None,
                                         None) == 0
+
+
+EWORKSPACE = header_define("MSS_EWORKSPACE")
+OP_SCAN_BWD = header_define("MSS_OP_SELECTIVE_SCAN_BACKWARD")
+OP_CONV_BWD = header_define("MSS_OP_CONV1D_SILU_BACKWARD")
+
+
+def ws_bytes(L, dims, op):
+    n = ctypes.c_size_t(123)
+    st = L.mss_workspace_bytes(ctypes.byref(dims) if dims is not None else None, op,
+                               ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_query(L):
+    assert (OP_SCAN_BWD, OP_CONV_BWD) == (mss.OP_SELECTIVE_SCAN_BACKWARD,
+                                          mss.OP_CONV1D_SILU_BACKWARD)
+    d = mss.make_dims(2, 512, 256, 16, 4)
+    st, n = ws_bytes(L, d, OP_SCAN_BWD)
+    # at least the checkpoints (8 floats per lane and block, 2 lanes per
+    # channel) and the per-tile dB / dC rows
+    assert st == 0 and n >= 2 * 512 * 256 * 2 * 4 + 2 * (2 * 8 * 512 * 16 * 4) and n % 256 == 0
+    st, n = ws_bytes(L, d, OP_CONV_BWD)
+    assert st == 0 and n > 0 and n % 256 == 0
+    assert ws_bytes(L, mss.make_dims(0, 512, 256, 16, 4), OP_SCAN_BWD) == (0, 0)
+    assert ws_bytes(L, mss.make_dims(2, 0, 256, 16, 4), OP_CONV_BWD) == (0, 0)
+    assert ws_bytes(L, d, 99)[0] == EINVAL
+    assert ws_bytes(L, None, OP_SCAN_BWD)[0] == EINVAL
+    assert ws_bytes(L, mss.make_dims(2, 512, 256, 17, 4), OP_SCAN_BWD)[0] == EINVAL
+    assert ws_bytes(L, mss.make_dims(2, 512, 256, 16, 9), OP_CONV_BWD)[0] == EINVAL
+    assert L.mss_workspace_bytes(ctypes.byref(d), OP_SCAN_BWD, None) == EINVAL
+
+
+def scan_bwd_call(L, dims, disc=0, ws_size=None, **over):
+    args = dict(u=fake(1), delta=fake(2), A_log=fake(3), B=fake(4), C=fake(5), D_vec=fake(6),
+                z=fake(7), h0=None, dout=fake(8), du=fake(9), ddelta=fake(10), dA_log=fake(11),
+                dB=fake(12), dC=fake(13), dD=fake(14), dz=fake(15), dh0=None, ws=fake(16))
+    args.update(over)
+    if ws_size is None:
+        ws_size = ws_bytes(L, dims, OP_SCAN_BWD)[1]
+    vals = list(args.values())
+    return L.mss_selective_scan_backward(ctypes.byref(dims), disc, *vals, ws_size, None)
+
+
+def test_scan_backward_validation(L):
+    d = mss.make_dims(2, 64, 64, 16, 4)
+    assert scan_bwd_call(L, d, disc=3) == EINVAL
+    for name in ("u", "delta", "A_log", "B", "C", "dout", "du", "ddelta", "dA_log", "dB", "dC"):
+        assert scan_bwd_call(L, d, **{name: None}) == EINVAL, name
+    assert scan_bwd_call(L, d, dz=None) == EINVAL                 # z given needs dz
+    assert scan_bwd_call(L, d, dout=ctypes.c_void_p(BASE + 8 * (1 << 32) + 4)) == EALIGN
+    assert scan_bwd_call(L, d, du=fake(1)) == EALIAS              # output on an input
+    assert scan_bwd_call(L, d, dB=fake(12), dC=fake(12)) == EALIAS
+    assert scan_bwd_call(L, d, ws=fake(9)) == EALIAS              # workspace on an output
+    assert scan_bwd_call(L, d, ws=None) == EWORKSPACE
+    need = ws_bytes(L, d, OP_SCAN_BWD)[1]
+    assert scan_bwd_call(L, d, ws_size=need - 1) == EWORKSPACE
+    assert scan_bwd_call(L, d, ws=ctypes.c_void_p(BASE + 16 * (1 << 32) + 16)) == EALIGN
+
+
+def conv_bwd_call(L, dims, ws_size=None, **over):
+    args = dict(x=fake(1), w=fake(2), b=fake(3), du=fake(4), dx=fake(5), dw=fake(6), db=fake(7),
+                ws=fake(8))
+    args.update(over)
+    if ws_size is None:
+        ws_size = ws_bytes(L, dims, OP_CONV_BWD)[1]
+    return L.mss_conv1d_silu_backward(ctypes.byref(dims), *args.values(), ws_size, None)
+
+
+def test_conv_backward_validation(L):
+    d = mss.make_dims(2, 64, 64, 1, 4)
+    for name in ("x", "w", "du", "dx", "dw"):
+        assert conv_bwd_call(L, d, **{name: None}) == EINVAL, name
+    assert conv_bwd_call(L, mss.make_dims(2, 64, 64, 1, 0)) == EINVAL
+    assert conv_bwd_call(L, d, dx=fake(1)) == EALIAS
+    assert conv_bwd_call(L, d, ws=None) == EWORKSPACE
+    assert conv_bwd_call(L, d, ws_size=1) == EWORKSPACE
+    assert conv_bwd_call(L, d, du=ctypes.c_void_p(BASE + 4 * (1 << 32) + 8)) == EALIGN
