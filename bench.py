@@ -124,6 +124,7 @@ def extras(w, d, y, disc, stream):
                                stream=stream)
 
     t64 = _time_ms(decode64, stream, 3, warm=1)
+    res["backward"] = backward_extras(w, d, stream)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
     step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
@@ -131,6 +132,45 @@ def extras(w, d, y, disc, stream):
                      "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
                      "note": "h + conv window (~100 MB) fit the 256 MB last-level cache"}
     return res
+
+
+def backward_extras(w, d, stream):
+    """The backward passes on the same workload (ZOH): the scan backward
+    (main kernel + fixed-order reduction kernel) on u = SiLU(conv(x)) with a
+    seeded N(0, 1) output gradient, then the conv1d + SiLU backward."""
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+    M, D, N = w.M, w.d_inner, w.d_state
+    u = mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch, seq_len=w.seq_len,
+                        stream=stream)
+    dout = torch.from_numpy(gen.cotangent(w)).cuda()
+    kw = dict(batch=w.batch, seq_len=w.seq_len, stream=stream)
+    nb = mss.workspace_bytes(mss.OP_SELECTIVE_SCAN_BACKWARD, batch=w.batch, seq_len=w.seq_len,
+                             d_inner=D, d_state=N)
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+    box = {}
+
+    def sb():
+        box["g"] = mss.selective_scan_backward(u, d["delta"], d["A_log"], d["B"], d["C"],
+                                               d["D_vec"], d["z"], None, dout, disc="zoh",
+                                               workspace=ws, **kw)
+    t_sb = _time_ms(sb, stream, 5)
+    du = box["g"]["du"]
+    nc = mss.workspace_bytes(mss.OP_CONV1D_SILU_BACKWARD, batch=w.batch, seq_len=w.seq_len,
+                             d_inner=D, d_state=1, d_conv=w.d_conv)
+    wsc = torch.empty(nc + 256, dtype=torch.uint8, device="cuda")
+    t_cb = _time_ms(lambda: mss.conv1d_silu_backward(d["x"], d["w_conv"], d["b_conv"], du,
+                                                     workspace=wsc, **kw), stream, 5)
+    # algorithmic bytes: u, delta, z, dout in and du, ddelta, dz out per (m, d);
+    # B, C in and dB, dC out per (m, n); x, du in and dx out for the conv
+    sb_bytes = 4 * (7 * M * D + 4 * M * N + 3 * D * N + 2 * D)
+    cb_bytes = 4 * (3 * M * D + 2 * D * (w.d_conv + 1))
+    return {"disc": "zoh", "workspace_bytes": nb,
+            "scan_backward_ms": t_sb, "scan_backward_algorithmic_bytes": sb_bytes,
+            "scan_backward_GBps": sb_bytes / t_sb / 1e6,
+            "conv1d_silu_backward_ms": t_cb, "conv1d_silu_backward_GBps": cb_bytes / t_cb / 1e6,
+            "total_ms": t_sb + t_cb}
 
 
 def cpu_baseline(w, inp, disc, target_s=15.0):

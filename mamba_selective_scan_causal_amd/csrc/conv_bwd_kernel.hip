@@ -14,7 +14,7 @@
 // and are written once per wave; a second kernel adds the waves of a channel
 // tile in a fixed order.
 #include "device_math.h"
-#include "launch.h"
+#include "launch_bwd.h"
 
 namespace mss {
 namespace {

@@ -75,67 +75,6 @@ struct StepArgs {
 
 hipError_t launch_step(const StepArgs& a, hipStream_t st);
 
-// Backward of the scan: one wave per (batch row, 32-channel tile, segment of
-// `seg` steps, a multiple of 8).  Workspace regions (all fp32):
-//   ckpt  (waves, blocks_per_seg, 64, 8)   h at every 8-step block start
-//   partB, partC (B, tiles_per_b, L, 16)    per-tile dB / dC rows
-//   partA (waves, 64, 8), partD (waves, 32) per-wave dA / dD sums
-struct BwdShape {
-    int64_t B, L, D;
-    int N;
-    int64_t tiles_per_b;      // ceil(D / 32)
-    int64_t nseg, seg, blocks_per_seg;
-    bool bc_vec;              // B and C rows 16-byte aligned (N = 16)
-};
-
-struct BwdArgs {
-    int disc;
-    const float* u;
-    const float* delta;
-    const float* A_log;
-    const float* B;
-    const float* C;
-    const float* D_vec;
-    const float* z;
-    const float* h0;
-    const float* dout;
-    float* du;
-    float* ddelta;
-    float* dA_log;
-    float* dB;
-    float* dC;
-    float* dD_vec;
-    float* dz;
-    float* dh0;
-    float* ckpt;
-    float* partB;
-    float* partC;
-    float* partA;
-    float* partD;
-};
-
-hipError_t launch_scan_bwd(const BwdArgs& a, const BwdShape& s, hipStream_t st);
-
-// Backward of conv1d + SiLU: one wave per (64-channel tile, group); group g
-// takes the (b, 32-step run) jobs g, g + groups, ...  Workspace: part
-// (tiles, groups, kMaxK + 1, 64) fp32, per-wave sums of dw (rows 0..K-1)
-// and db (row K).
-struct ConvBwdArgs {
-    int64_t B, L, D;
-    int K;
-    int64_t groups;
-    const float* x;
-    const float* w_conv;
-    const float* b_conv;
-    const float* du;
-    float* dx;
-    float* dw;
-    float* db;
-    float* part;
-};
-
-hipError_t launch_conv1d_silu_bwd(const ConvBwdArgs& a, hipStream_t st);
-
 // h_last for a zero-length sequence: h0 copied, or zeros.
 hipError_t launch_state_init(const float* h0, float* h_last, int64_t count, hipStream_t st);
 

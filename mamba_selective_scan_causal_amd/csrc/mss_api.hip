@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "launch_bwd.h"
 #include "mss.h"
 
 namespace {

@@ -35,7 +35,7 @@
 // and dD are written per wave and summed the same way.  No atomics: the
 // result is bitwise reproducible.
 #include "device_math.h"
-#include "launch.h"
+#include "launch_bwd.h"
 
 namespace mss {
 namespace {
@@ -46,8 +46,7 @@ constexpr int kBackBlk = 16;
 constexpr float kDecayCut = 30.0f;
 constexpr float kSmallX = 0.015625f;           // expm1 cubic below |dv A| = 2^-6
 constexpr float kSmallX2 = kSmallX * kLog2e;
-constexpr float kPhiX = 0.125f;                // ZOH dA series below |dv A| = 1/8
-constexpr float kPhiX2 = kPhiX * kLog2e;
+constexpr int kNone = 0, kFirst = 1, kAll = 2;  // which states take the accurate path
 
 struct BwdCols {
     const float* __restrict__ u;
@@ -213,93 +212,136 @@ struct Bwd {
     }
 
     // ---- forward state update (as the forward kernel) -------------------
+    // SLOW: the decay is applied as h + m h with m = expm1(dv A) accurate
+    // (cubic below |dv A| = 2^-6), since fl(aBar) next to 1 carries an
+    // absolute error that would compound over a long memory.
     template <bool SLOW>
-    __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv, const float (&Bv)[kH]) const {
-        const float dvu = dv * uv;
-#pragma unroll
-        for (int j = 0; j < kH; j++) {
-            if (!valid(j)) continue;
-            const float x2 = dv * A2[j];
-            const float a = ex2(x2);
-            if constexpr (!SLOW) {
-                if constexpr (kZoh) {
-                    const float k = (uv * Ai[j]) * Bv[j];
-                    h[j] = __builtin_fmaf(a, h[j] + k, -k);
-                } else {
-                    h[j] = __builtin_fmaf(a, h[j], dvu * Bv[j]);
-                }
+    __device__ __forceinline__ void fwd_state(int j, float& h, float uv, float dv, float dvu,
+                                              float Bj) const {
+        const float x2 = dv * A2[j];
+        const float a = ex2(x2);
+        if constexpr (!SLOW) {
+            if constexpr (kZoh) {
+                const float k = (uv * Ai[j]) * Bj;
+                h = __builtin_fmaf(a, h + k, -k);
             } else {
-                const float m = em1_of(x2 * kLn2, a);
-                if constexpr (kZoh) {
-                    const float k = (uv * Ai[j]) * Bv[j];
-                    h[j] = __builtin_fmaf(m, h[j] + k, h[j]);
-                } else {
-                    h[j] = __builtin_fmaf(dvu, Bv[j], __builtin_fmaf(m, h[j], h[j]));
-                }
+                h = __builtin_fmaf(a, h, dvu * Bj);
+            }
+        } else {
+            const float m = em1_of(x2 * kLn2, a);
+            if constexpr (kZoh) {
+                const float k = (uv * Ai[j]) * Bj;
+                h = __builtin_fmaf(m, h + k, h);
+            } else {
+                h = __builtin_fmaf(dvu, Bj, __builtin_fmaf(m, h, h));
             }
         }
     }
 
+    // SM (slow mode of the block, see slow_mode): kNone, kFirst (state 0
+    // takes the accurate path) or kAll.
+    template <int SM>
+    static constexpr bool slow_state(int j) {
+        return SM == kAll || (SM == kFirst && j == 0);
+    }
+
+    template <int SM>
+    __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv,
+                                        const float (&Bv)[kH]) const {
+        const float dvu = dv * uv;
+#pragma unroll
+        for (int j = 0; j < kH; j++) {
+            if (!valid(j)) continue;
+            if (slow_state<SM>(j))
+                fwd_state<true>(j, h[j], uv, dv, dvu, Bv[j]);
+            else
+                fwd_state<false>(j, h[j], uv, dv, dvu, Bv[j]);
+        }
+    }
+
     // ---- reverse (adjoint) step ------------------------------------------
-    // FULL: also the gradients (du, ddv, dA, dB terms); otherwise only g.
+    // FULL: also the gradient terms (du, ddv, dA, dB); otherwise only g.
+    // With dh = C dY + g and gn = aBar dh (the adjoint passed to step t-1):
+    //   ZOH (q = (aBar-1)/A, K = u B / A):
+    //     du += dh q B,  dB term = dh q u,  ddv += gn (h_{t-1} A + u B),
+    //     dA += dh (dv aBar (h_{t-1} + K) - K q)
+    //   EULER: du += dh dv B,  dB term = dh u dv,
+    //     ddv += gn h_{t-1} A + dh u B,  dA += gn dv h_{t-1}
+    // SLOW (some lane has |dv A| < 2^-6): m = aBar - 1 from its cubic, gn as
+    // dh + m dh, and for ZOH the dA term as dv aBar h_{t-1} + K t5 with
+    // t5 = dv aBar - q from its series dv x (1/2 + x/3 + x^2/8 + x^3/30)
+    // (x = dv A) where |x| < 2^-6: the direct difference cancels there.
     template <bool SLOW, bool FULL>
+    __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float uv,
+                                              float dv, float udv, float dY, float Bj, float Cj,
+                                              float& du_acc, float& ddv_acc, float& dBp) const {
+        const float x2 = dv * A2[j];
+        const float a = ex2(x2);
+        const float dh = __builtin_fmaf(Cj, dY, g);
+        float m = 0.0f, gn;
+        if constexpr (SLOW) {
+            m = em1_of(x2 * kLn2, a);
+            gn = __builtin_fmaf(m, dh, dh);
+        } else {
+            gn = dh * a;
+        }
+        g = gn;
+        if constexpr (FULL) {
+            if constexpr (kZoh) {
+                if constexpr (!SLOW) m = a - 1.0f;
+                const float q = m * Ai[j];
+                const float dq = dh * q;
+                du_acc = __builtin_fmaf(dq, Bj, du_acc);
+                dBp = dq * uv;
+                const float uB = uv * Bj;
+                const float K = uB * Ai[j];
+                ddv_acc = __builtin_fmaf(gn, __builtin_fmaf(hp, An[j], uB), ddv_acc);
+                float inner;
+                if constexpr (!SLOW) {
+                    inner = __builtin_fmaf(dv, a * (hp + K), -(K * q));
+                } else {
+                    const float x = x2 * kLn2;
+                    const float ph = __builtin_fmaf(
+                        x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f),
+                        0.5f);
+                    const float t5d = __builtin_fmaf(dv, a, -q);
+                    const float t5 = __builtin_fabsf(x) < kSmallX ? (dv * x) * ph : t5d;
+                    inner = __builtin_fmaf(dv * a, hp, K * t5);
+                }
+                dA = __builtin_fmaf(dh, inner, dA);
+            } else {
+                du_acc = __builtin_fmaf(dh, dv * Bj, du_acc);
+                dBp = dh * udv;
+                ddv_acc = __builtin_fmaf(gn, hp * An[j], ddv_acc);
+                ddv_acc = __builtin_fmaf(dh, uv * Bj, ddv_acc);
+                dA = __builtin_fmaf(gn, dv * hp, dA);
+            }
+        }
+    }
+
+    template <int SM, bool FULL>
     __device__ __forceinline__ void rev(float (&g)[kH], float (&dA)[kH], const float (&hp)[kH],
                                         float uv, float dv, float dY, const float (&Bv)[kH],
                                         const float (&Cv)[kH], float& du_acc, float& ddv_acc,
                                         float (&dBp)[kH]) const {
+        const float udv = uv * dv;
 #pragma unroll
         for (int j = 0; j < kH; j++) {
             if (!valid(j)) {
                 if constexpr (FULL) dBp[j] = 0.0f;
                 continue;
             }
-            const float x2 = dv * A2[j];
-            const float a = ex2(x2);
-            const float dh = __builtin_fmaf(Cv[j], dY, g[j]);
-            float m = 0.0f;
-            if constexpr (SLOW) {
-                m = em1_of(x2 * kLn2, a);
-                g[j] = __builtin_fmaf(m, dh, dh);
-            } else {
-                g[j] = dh * a;
-            }
-            if constexpr (FULL) {
-                const float dab = dh * hp[j];
-                const float dbb = dh * uv;
-                if constexpr (kZoh) {
-                    if constexpr (!SLOW) m = a - 1.0f;
-                    const float q = m * Ai[j];                     // (aBar - 1) / A
-                    du_acc = __builtin_fmaf(dh, q * Bv[j], du_acc);
-                    dBp[j] = dbb * q;
-                    const float wv = dbb * Bv[j];
-                    ddv_acc = __builtin_fmaf(a, __builtin_fmaf(dab, An[j], wv), ddv_acc);
-                    // (dv aBar A - (aBar - 1)) / A^2 = Ai (dv aBar - q); below
-                    // |dv A| = 1/8 that difference cancels and is taken from
-                    // its series dv x (1/2 + x/3 + x^2/8 + x^3/30), x = dv A.
-                    float t5 = __builtin_fmaf(dv, a, -q);
-                    if constexpr (SLOW) {
-                        const float x = x2 * kLn2;
-                        const float ph = __builtin_fmaf(
-                            x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f),
-                            0.5f);
-                        t5 = __builtin_fabsf(x) < kPhiX ? (dv * x) * ph : t5;
-                    }
-                    dA[j] = __builtin_fmaf(dv, a * dab, dA[j]);
-                    dA[j] = __builtin_fmaf(wv * Ai[j], t5, dA[j]);
-                } else {
-                    du_acc = __builtin_fmaf(dh, dv * Bv[j], du_acc);
-                    dBp[j] = dbb * dv;
-                    const float ad = a * dab;
-                    ddv_acc = __builtin_fmaf(ad, An[j], ddv_acc);
-                    ddv_acc = __builtin_fmaf(dbb, Bv[j], ddv_acc);
-                    dA[j] = __builtin_fmaf(dv, ad, dA[j]);
-                }
-            }
+            if (slow_state<SM>(j))
+                rev_state<true, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
+                                      du_acc, ddv_acc, dBp[j]);
+            else
+                rev_state<false, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
+                                       du_acc, ddv_acc, dBp[j]);
         }
     }
 
     // ---- decay-bounded replay bounds --------------------------------------
-    __device__ int64_t replay_start(int64_t t0) const {
+    __device__ __forceinline__ int64_t replay_start(int64_t t0) const {
         if (t0 == 0) return 0;
         float S = 0.0f;
         int64_t t = t0;
@@ -322,7 +364,7 @@ struct Bwd {
     }
 
     // End (exclusive) of the reverse replay that carries the adjoint into t1-1.
-    __device__ int64_t replay_end(int64_t t1) const {
+    __device__ __forceinline__ int64_t replay_end(int64_t t1) const {
         if (t1 >= L) return L;
         float S = 0.0f;
         int64_t t = t1;
@@ -344,28 +386,26 @@ struct Bwd {
         }
     }
 
-    // Block choice.  Forward-type passes: as the forward kernel (every lane's
-    // slowest state decays by at least exp(-8 2^-6) over the block).  Reverse
-    // passes, ZOH: every step of the block has |dv A| >= 1/8 in every state
-    // (the dA term needs no series); EULER: as the forward passes.
-    __device__ __forceinline__ bool slow_fwd(const float (&dv)[kT], int n) const {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kT; i++) s += i < n ? dv[i] : 0.0f;
-        return wave_any(s * min_a2 < n * kSmallX2);
-    }
-    __device__ __forceinline__ bool slow_rev(const float (&dv)[kT], int n) const {
-        if constexpr (!kZoh) return slow_fwd(dv, n);
+    // A state needs the accurate path in a block when some lane has
+    // |dv A| < 2^-6 at some step of it.  The block then runs kNone (no such
+    // state), kFirst (only state 0: with A ordered by magnitude, as in the
+    // S4D initialisation, state 0 holds the slowest mode) or kAll.
+    __device__ __forceinline__ int slow_mode(const float (&dv)[kT], int n) const {
         float mn = 3.0e38f;
 #pragma unroll
         for (int i = 0; i < kT; i++) mn = i < n ? __builtin_fminf(mn, dv[i]) : mn;
-        return wave_any(mn * min_a2 < kPhiX2);
+        bool rest = false;
+#pragma unroll
+        for (int j = 1; j < kH; j++)
+            if (valid(j)) rest = rest || (mn * -A2[j] < kSmallX2);
+        if (wave_any(rest)) return kAll;
+        return wave_any(mn * -A2[0] < kSmallX2) ? kFirst : kNone;
     }
 
     // ---- forward sweep over [ta, tb) in blocks of 8 from ta ---------------
     // CKPT: store h at every block start to ck (2 KB per block, lane-major).
     template <bool CKPT>
-    __device__ void fwd_sweep(float (&h)[kH], int64_t ta, int64_t tb, float* ck) const {
+    __device__ __forceinline__ void fwd_sweep(float (&h)[kH], int64_t ta, int64_t tb, float* ck) const {
         for (int64_t s = ta; s < tb; s += kT) {
             const int n = tb - s < kT ? static_cast<int>(tb - s) : kT;
             if constexpr (CKPT) {
@@ -384,23 +424,13 @@ struct Bwd {
             stage(s);
 #pragma unroll
             for (int i = 0; i < kT; i++) dv[i] = softplus(dv[i]);
-            if (!slow_fwd(dv, n)) {
-#pragma unroll
-                for (int i = 0; i < kT; i++) {
-                    if (i >= n) break;
-                    float Bv[kH];
-                    read_row(0, i, Bv);
-                    fwd<false>(h, uu[i], dv[i], Bv);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < kT; i++) {
-                    if (i >= n) break;
-                    float Bv[kH];
-                    read_row(0, i, Bv);
-                    fwd<true>(h, uu[i], dv[i], Bv);
-                }
-            }
+            const int sm = slow_mode(dv, n);
+            if (sm == kNone)
+                fwd_block<kNone>(h, uu, dv, n);
+            else if (sm == kFirst)
+                fwd_block<kFirst>(h, uu, dv, n);
+            else
+                fwd_block<kAll>(h, uu, dv, n);
         }
     }
 
@@ -410,8 +440,34 @@ struct Bwd {
         return live ? v : 0.0f;
     }
 
+    template <int SM>
+    __device__ __forceinline__ void fwd_block(float (&h)[kH], const float (&uu)[kT],
+                                              const float (&dv)[kT], int n) const {
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            if (i >= n) break;
+            float Bv[kH];
+            read_row(0, i, Bv);
+            fwd<SM>(h, uu[i], dv[i], Bv);
+        }
+    }
+
+    // Only g is updated; the gradient arguments of rev are not read.
+    template <int SM>
+    __device__ __forceinline__ void rev_block(float (&g)[kH], const float (&dv)[kT],
+                                              const float (&dY)[kT], int n) const {
+        float dA[kH] = {}, hp[kH] = {}, dBp[kH], Bv[kH] = {}, du_acc = 0.0f, ddv_acc = 0.0f;
+#pragma unroll
+        for (int i = kT - 1; i >= 0; i--) {
+            if (i >= n) continue;
+            float Cv[kH];
+            read_row(32, i, Cv);
+            rev<SM, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+        }
+    }
+
     // ---- reverse replay over [ta, tb), adjoint only -----------------------
-    __device__ void rev_sweep(float (&g)[kH], int64_t ta, int64_t tb) const {
+    __device__ __forceinline__ void rev_sweep(float (&g)[kH], int64_t ta, int64_t tb) const {
         const int64_t nb = (tb - ta + kT - 1) / kT;
         for (int64_t k = nb - 1; k >= 0; k--) {
             const int64_t s = ta + k * kT;
@@ -428,30 +484,18 @@ struct Bwd {
             stage(s);
 #pragma unroll
             for (int i = 0; i < kT; i++) dv[i] = softplus(dv[i]);
-            // Only g is updated; the gradient arguments are not read.
-            float dA[kH] = {}, hp[kH] = {}, dBp[kH], Bv[kH] = {}, du_acc = 0.0f, ddv_acc = 0.0f;
-            if (!slow_rev(dv, n)) {
-#pragma unroll
-                for (int i = kT - 1; i >= 0; i--) {
-                    if (i >= n) continue;
-                    float Cv[kH];
-                    read_row(32, i, Cv);
-                    rev<false, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
-                }
-            } else {
-#pragma unroll
-                for (int i = kT - 1; i >= 0; i--) {
-                    if (i >= n) continue;
-                    float Cv[kH];
-                    read_row(32, i, Cv);
-                    rev<true, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
-                }
-            }
+            const int sm = slow_mode(dv, n);
+            if (sm == kNone)
+                rev_block<kNone>(g, dv, dY, n);
+            else if (sm == kFirst)
+                rev_block<kFirst>(g, dv, dY, n);
+            else
+                rev_block<kAll>(g, dv, dY, n);
         }
     }
 
     // ---- one block of the main pass ---------------------------------------
-    template <bool SLOW>
+    template <int SM>
     __device__ __forceinline__ void block(float (&g)[kH], float (&dA)[kH], float& dD,
                                           const float (&h_in)[kH], int64_t s, int n,
                                           const float (&uu)[kT], const float (&dl)[kT],
@@ -472,7 +516,7 @@ struct Bwd {
             float Bv[kH], Cv[kH];
             read_row(0, i, Bv);
             read_row(32, i, Cv);
-            fwd<SLOW>(h, uu[i], dv[i], Bv);
+            fwd<SM>(h, uu[i], dv[i], Bv);
             if (i + 1 < kT) {
 #pragma unroll
                 for (int j = 0; j < kH; j++) hist[i + 1][j] = h[j];
@@ -498,7 +542,7 @@ struct Bwd {
             read_row(0, i, Bv);
             read_row(32, i, Cv);
             float du_acc = 0.0f, ddv_acc = 0.0f;
-            rev<SLOW, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+            rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
             const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
             const float ddv = pair_sum(ddv_acc);
             const int64_t r = row(s + i);
@@ -575,12 +619,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         bw.stage(st);
 #pragma unroll
         for (int i = 0; i < kT; i++) dv[i] = softplus(dl[i]);
-        // The reverse criterion implies the forward one (ZOH: every step has
-        // |dv A| >= 1/8; EULER: the two are the same).
-        if (!bw.slow_rev(dv, n))
-            bw.template block<false>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
+        const int sm = bw.slow_mode(dv, n);
+        if (sm == kNone)
+            bw.template block<kNone>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
+        else if (sm == kFirst)
+            bw.template block<kFirst>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
         else
-            bw.template block<true>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
+            bw.template block<kAll>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
     }
 
     // 5. per-wave partial sums and dh0
