@@ -134,7 +134,7 @@ def extras(w, d, y, disc, stream):
     return res
 
 
-def backward_extras(w, d, stream):
+def backward_extras(w, d, stream, reps=5):
     """The backward passes on the same workload (ZOH): the scan backward
     (main kernel + fixed-order reduction kernel) on u = SiLU(conv(x)) with a
     seeded N(0, 1) output gradient, then the conv1d + SiLU backward."""
@@ -155,13 +155,13 @@ def backward_extras(w, d, stream):
         box["g"] = mss.selective_scan_backward(u, d["delta"], d["A_log"], d["B"], d["C"],
                                                d["D_vec"], d["z"], None, dout, disc="zoh",
                                                workspace=ws, **kw)
-    t_sb = _time_ms(sb, stream, 5)
+    t_sb = _time_ms(sb, stream, reps)
     du = box["g"]["du"]
     nc = mss.workspace_bytes(mss.OP_CONV1D_SILU_BACKWARD, batch=w.batch, seq_len=w.seq_len,
                              d_inner=D, d_state=1, d_conv=w.d_conv)
     wsc = torch.empty(nc + 256, dtype=torch.uint8, device="cuda")
     t_cb = _time_ms(lambda: mss.conv1d_silu_backward(d["x"], d["w_conv"], d["b_conv"], du,
-                                                     workspace=wsc, **kw), stream, 5)
+                                                     workspace=wsc, **kw), stream, reps)
     # algorithmic bytes: u, delta, z, dout in and du, ddelta, dz out per (m, d);
     # B, C in and dB, dC out per (m, n); x, du in and dx out for the conv
     sb_bytes = 4 * (7 * M * D + 4 * M * N + 3 * D * N + 2 * D)
@@ -211,6 +211,9 @@ def main():
                     help="skip the side measurements (other mode, unfused path, decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--part", default="all", choices=("all", "backward"),
+                    help="backward: only the backward passes on the same workload "
+                         "(one JSON line of their timings, for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
@@ -228,6 +231,11 @@ def main():
     w = gen.MAMBA_2P8B
     inp = gen.generate(w)
     d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    if args.part == "backward":
+        res = backward_extras(w, d, torch.cuda.current_stream(), reps=max(args.steps, 1))
+        res["workload"] = w.name
+        print(json.dumps(res))
+        return
     y = torch.empty((w.M, w.d_inner), device="cuda")
     stream = torch.cuda.current_stream()
 
