@@ -171,3 +171,57 @@ def cotangent(w: Workload, seed_offset: int = 0, threads: int = 8) -> np.ndarray
     from a stream of its own (the inputs of ``generate`` are unchanged)."""
     seq = np.random.SeedSequence([SEED_BASE + w.seed_index + 1000 * seed_offset, 0xD07])
     return _normal(seq, (w.M, w.d_inner), 0.0, 1.0, threads)
+
+
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    """Shape and value recipe of a Mamba-2 SSD scan workload: H heads of P
+    channels, G groups of N states.  x ~ N(0, 1); raw dt ~ N(dt_mean, dt_var)
+    per (row, head); A_log = log(U[1, 16]) per head; B, C ~ N(0, 1);
+    D ~ U(0.5, 1.5); dt_bias = 0; optional h0 ~ N(0, 0.1)."""
+    name: str
+    batch: int
+    seq_len: int
+    n_heads: int
+    head_dim: int
+    d_state: int
+    n_groups: int = 1
+    dt_mean: float = -2.0
+    dt_var: float = 0.5
+    h0: bool = False
+    seed_index: int = 20
+
+    @property
+    def M(self) -> int:
+        return self.batch * self.seq_len
+
+    def with_(self, **kw) -> "SsdWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+SSD_TINY = SsdWorkload("ssd_b1_l100_h4_p16_n32_g2", 1, 100, 4, 16, 32, n_groups=2, h0=True,
+                       seed_index=21)
+SSD_SMALL = SsdWorkload("ssd_b2_l512_h8_p64_n128_g1", 2, 512, 8, 64, 128, h0=True,
+                        seed_index=22)
+SSD_2P7B = SsdWorkload("ssd_b4_l8192_h80_p64_n128_g1", 4, 8192, 80, 64, 128, seed_index=23)
+
+_SSD_STREAMS = ("x", "dt", "A_log", "B", "C", "D_vec", "h0")
+
+
+def generate_ssd(w: SsdWorkload, seed_offset: int = 0, threads: int = 8) -> dict:
+    """Draw every input of SSD workload ``w`` (fp32, C-contiguous)."""
+    ss = np.random.SeedSequence([SEED_BASE + w.seed_index + 1000 * seed_offset, 0x55D])
+    ch = dict(zip(_SSD_STREAMS, ss.spawn(len(_SSD_STREAMS))))
+    H, P, N, G = w.n_heads, w.head_dim, w.d_state, w.n_groups
+    out = {
+        "x": _normal(ch["x"], (w.M, H * P), 0.0, 1.0, threads),
+        "dt": _normal(ch["dt"], (w.M, H), w.dt_mean, w.dt_var, threads),
+        "A_log": np.log(_uniform(ch["A_log"], (H,), 1.0, 16.0)).astype(np.float32),
+        "B": _normal(ch["B"], (w.M, G * N), 0.0, 1.0, threads),
+        "C": _normal(ch["C"], (w.M, G * N), 0.0, 1.0, threads),
+        "D_vec": _uniform(ch["D_vec"], (H,), 0.5, 1.5),
+        "dt_bias": np.zeros(H, dtype=np.float32),
+    }
+    if w.h0:
+        out["h0"] = _normal(ch["h0"], (w.batch, H, P, N), 0.0, 0.1, threads)
+    return out

@@ -527,4 +527,64 @@ int oracle_conv1d_silu_backward(int64_t B, int64_t L, int64_t D, int64_t K,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Mamba-2 state-space-dual scan (the recurrence that the pages' Mamba2Block
+ * dispatches as ssd_chunk_forward, same package, src/model/mamba2_block.ts;
+ * the pages show its buffers but not its arithmetic).  Plainest reading,
+ * consistent with the Mamba-1 path of the same pages:
+ *   H heads of P channels (x column h*P + p), G groups of N states sharing
+ *   B and C (head h uses group h / (H / G), column g*N + n);
+ *   dv = softplus(dt[r, h] + dt_bias[h]),  A_h = -exp(clamp(A_log[h], -10, 5))
+ *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + dv x[r, h*P + p] B[r, g*N + n]
+ *   y[r, h*P + p] = sum_n C[r, g*N + n] S_h[p, n] + D[h] x[r, h*P + p]
+ * State (B, H, P, N), starting at h0 or 0.  One (b, h) at a time, time in
+ * order, fp64.                                                              */
+int oracle_ssd_scan(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                    const float* x, const float* dt, const float* A_log, const float* Bm,
+                    const float* Cm, const float* Dv, const float* dt_bias, const float* h0,
+                    double* y, double* h_last, int nthreads) {
+    if (B < 0 || L < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return -1;
+    if (!x || !dt || !A_log || !Bm || !Cm || !y) return -1;
+    const int64_t HP = H * P, GN = G * N, hpg = H / G;
+    int nt = set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+        if (!S) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; bh++) {
+            if (!S) continue;
+            const int64_t b = bh / H, h = bh % H, g = h / hpg;
+            const double A = a_cont((double)A_log[h]);
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            const double Dh = Dv ? (double)Dv[h] : 0.0;
+            for (int64_t i = 0; i < P * N; i++)
+                S[i] = h0 ? (double)h0[bh * P * N + i] : 0.0;
+            for (int64_t t = 0; t < L; t++) {
+                const int64_t r = b * L + t;
+                const double dv = softplus((double)dt[r * H + h] + bias);
+                const double a = exp(dv * A);
+                for (int64_t p = 0; p < P; p++) {
+                    const double xv = (double)x[r * HP + h * P + p];
+                    double acc = Dh * xv;
+                    for (int64_t n = 0; n < N; n++) {
+                        double* s = &S[p * N + n];
+                        *s = a * *s + dv * xv * (double)Bm[r * GN + g * N + n];
+                        acc += (double)Cm[r * GN + g * N + n] * *s;
+                    }
+                    y[r * HP + h * P + p] = acc;
+                }
+            }
+            if (h_last)
+                for (int64_t i = 0; i < P * N; i++) h_last[bh * P * N + i] = S[i];
+        }
+        free(S);
+    }
+    return err;
+}
+
 int oracle_abi_version(void) { return 1; }

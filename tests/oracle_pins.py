@@ -645,4 +645,134 @@ def pin_conv_backward_finite_differences(orc):
                 f"conv d/d{nm}{idx}: oracle {grad[idx]:.10e} vs finite difference {fd:.10e}")
 
 
+# --------------------------------------------------------------------------
+# Mamba-2 SSD scan
+
+
+def _ssd_inputs(seed, B, L, H, P, N, G, *, h0=True, bias=True):
+    g = _rng(seed)
+    return dict(
+        x=_f32(g.standard_normal((B * L, H * P))),
+        dt=_f32(g.standard_normal((B * L, H)) - 1.0),
+        A_log=_f32(g.uniform(-1.0, 2.5, H)),
+        B=_f32(g.standard_normal((B * L, G * N))),
+        C=_f32(g.standard_normal((B * L, G * N))),
+        D_vec=_f32(g.uniform(0.5, 1.5, H)),
+        dt_bias=_f32(g.uniform(-0.5, 0.5, H)) if bias else None,
+        h0=_f32(0.3 * g.standard_normal((B, H, P, N))) if h0 else None,
+    )
+
+
+def _ssd(orc, inp, B, L, H, P, N, G, **kw):
+    return orc.ssd_scan(inp["x"], inp["dt"], inp["A_log"], inp["B"], inp["C"], inp["D_vec"],
+                        inp["dt_bias"], inp["h0"], batch=B, seq_len=L, n_heads=H, head_dim=P,
+                        d_state=N, n_groups=G, h_last=True, **kw)
+
+
+def pin_ssd_is_mamba1_euler_per_channel(orc):
+    # Channel (h, p) of the SSD scan is the Mamba-1 EULER scan of one channel
+    # whose N states all have A_h, on delta = dt + dt_bias, with the B and C
+    # of the head's group: run the (separately pinned) Mamba-1 oracle group by
+    # group and compare y and the final state.
+    B, L, H, P, N, G = 2, 23, 6, 3, 5, 3
+    inp = _ssd_inputs(61, B, L, H, P, N, G)
+    y, hl = _ssd(orc, inp, B, L, H, P, N, G)
+    hpg = H // G
+    for g in range(G):
+        heads = range(g * hpg, (g + 1) * hpg)
+        cols = [h * P + p for h in heads for p in range(P)]
+        delta = np.concatenate([np.repeat((inp["dt"][:, h].astype(np.float64) +
+                                           inp["dt_bias"][h])[:, None], P, axis=1)
+                                for h in heads], axis=1)
+        # delta is rounded to fp32 on the way into the Mamba-1 oracle; keep
+        # only inputs where that is exact by comparing with a tolerance
+        alog = np.repeat(np.repeat(inp["A_log"][list(heads)], P)[:, None], N, axis=1)
+        y1, _, hl1 = orc.selective_scan(
+            inp["x"][:, cols], _f32(delta), _f32(alog), inp["B"][:, g * N:(g + 1) * N],
+            inp["C"][:, g * N:(g + 1) * N], np.repeat(inp["D_vec"][list(heads)], P), None,
+            inp["h0"][:, list(heads)].reshape(B, hpg * P, N), batch=B, seq_len=L,
+            disc=EULER, h_last=True)
+        _close(y[:, cols], y1, 1e-6, 1e-6, f"ssd vs mamba1, group {g}")
+        _close(hl[:, list(heads)].reshape(B, hpg * P, N), hl1, 1e-6, 1e-6,
+               f"ssd h_last vs mamba1, group {g}")
+
+
+def pin_ssd_exact_shift_of_dt(orc):
+    # With dt and dt_bias on a coarse dyadic grid, dt + dt_bias is exact in
+    # fp32, so adding the bias inside equals adding it outside, bitwise.
+    B, L, H, P, N, G = 1, 17, 4, 2, 3, 2
+    inp = _ssd_inputs(62, B, L, H, P, N, G)
+    inp["dt"] = _f32(np.round(inp["dt"] * 64) / 64)
+    inp["dt_bias"] = _f32(np.round(inp["dt_bias"] * 64) / 64)
+    y, hl = _ssd(orc, inp, B, L, H, P, N, G)
+    moved = dict(inp, dt=_f32(inp["dt"] + inp["dt_bias"][None, :]), dt_bias=None)
+    y2, hl2 = _ssd(orc, moved, B, L, H, P, N, G)
+    assert np.array_equal(y, y2) and np.array_equal(hl, hl2)
+
+
+def pin_ssd_quadratic_form(orc):
+    # The scan equals its unrolled (attention-like) form, evaluated here
+    # directly in fp64 for every output:
+    #   y[t,h,p] = sum_{s<=t} (C_t . B_s) exp(A_h sum_{r=s+1..t} dv_r) dv_s x[s,h,p]
+    #              + sum_n C_t,n exp(A_h sum_{r<=t} dv_r) h0[h,p,n] + D_h x[t,h,p]
+    B, L, H, P, N, G = 2, 12, 4, 3, 4, 2
+    inp = _ssd_inputs(63, B, L, H, P, N, G)
+    y, hl = _ssd(orc, inp, B, L, H, P, N, G)
+    hpg = H // G
+    want = np.zeros((B * L, H * P))
+    for b in range(B):
+        for h in range(H):
+            g = h // hpg
+            A = -np.exp(np.clip(np.float64(inp["A_log"][h]), -10.0, 5.0))
+            dv = _softplus(inp["dt"][b * L:(b + 1) * L, h].astype(np.float64) + inp["dt_bias"][h])
+            cum = np.concatenate([[0.0], np.cumsum(dv)])      # cum[t+1] = sum_{r<=t} dv_r
+            Bg = inp["B"][b * L:(b + 1) * L, g * N:(g + 1) * N].astype(np.float64)
+            Cg = inp["C"][b * L:(b + 1) * L, g * N:(g + 1) * N].astype(np.float64)
+            xs = inp["x"][b * L:(b + 1) * L, h * P:(h + 1) * P].astype(np.float64)
+            for t in range(L):
+                acc = inp["D_vec"][h] * xs[t]
+                for s_ in range(t + 1):
+                    acc = acc + (Cg[t] @ Bg[s_]) * np.exp(A * (cum[t + 1] - cum[s_ + 1])) * dv[s_] * xs[s_]
+                acc = acc + np.exp(A * cum[t + 1]) * (inp["h0"][b, h].astype(np.float64) @ Cg[t])
+                want[b * L + t, h * P:(h + 1) * P] = acc
+    _close(y, want, 1e-12, 1e-12, "ssd quadratic form")
+
+
+def pin_ssd_clamp_and_groups(orc):
+    # A_log beyond the clamp: same output bitwise; heads of one group with
+    # identical inputs give identical outputs; groups do not leak.
+    B, L, H, P, N, G = 1, 15, 4, 2, 3, 2
+    inp = _ssd_inputs(64, B, L, H, P, N, G)
+    inp["A_log"][0] = -10.0
+    inp["A_log"][1] = 5.0
+    y, _ = _ssd(orc, inp, B, L, H, P, N, G)
+    far = dict(inp, A_log=inp["A_log"].copy())
+    far["A_log"][0] = -30.0
+    far["A_log"][1] = 40.0
+    y2, _ = _ssd(orc, far, B, L, H, P, N, G)
+    assert np.array_equal(y, y2)
+    same = dict(inp)
+    for k_ in ("x",):
+        a = inp[k_].copy()
+        a[:, P:2 * P] = a[:, 0:P]
+        same[k_] = a
+    for k_ in ("dt",):
+        a = inp[k_].copy()
+        a[:, 1] = a[:, 0]
+        same[k_] = a
+    for k_ in ("A_log", "D_vec", "dt_bias"):
+        a = inp[k_].copy()
+        a[1] = a[0]
+        same[k_] = a
+    same["h0"] = inp["h0"].copy()
+    same["h0"][:, 1] = same["h0"][:, 0]
+    y3, _ = _ssd(orc, same, B, L, H, P, N, G)
+    assert np.array_equal(y3[:, 0:P], y3[:, P:2 * P])
+    other = dict(same, B=same["B"].copy())
+    other["B"][:, N:] += 1.0          # group 1 only: heads 2, 3
+    y4, _ = _ssd(orc, other, B, L, H, P, N, G)
+    assert np.array_equal(y4[:, :2 * P], y3[:, :2 * P])
+    assert not np.allclose(y4[:, 2 * P:], y3[:, 2 * P:])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
