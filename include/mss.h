@@ -216,6 +216,36 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
                              float* db_conv, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* ---- Mamba-2 SSD scan --------------------------------------------------------
+ * The recurrence that the pages' Mamba2Block dispatches as ssd_chunk_forward
+ * (diff 2026.7.14 -> 2026.9.28, src/model/mamba2_block.ts: x (M, D = H*P),
+ * dt (M, H), B and C (M, G*N) split from the projections).  The pages do not
+ * show its arithmetic; this is the plainest reading consistent with the
+ * Mamba-1 path: per batch row and head h of group g = h / (H/G),
+ *   dv = softplus(dt[r, h] + dt_bias[h]),  A_h = -exp(clamp(A_log[h], -10, 5))
+ *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + dv x[r, h*P + p] B[r, g*N + n]
+ *   y[r, h*P + p] = sum_n C[r, g*N + n] S_h[p, n] + D_vec[h] x[r, h*P + p]
+ * Computed in chunks on the matrix cores (fp32 MFMA); segments processed in
+ * parallel drop contributions that have decayed by more than 2^-30. */
+typedef struct mss_ssd_dims {
+    int32_t struct_size;    /* sizeof(mss_ssd_dims) */
+    int32_t reserved;       /* must be 0 */
+    int64_t batch;          /* B */
+    int64_t seq_len;        /* L */
+    int64_t n_heads;        /* H */
+    int64_t head_dim;       /* P: 16, 32, 64 or 128 */
+    int64_t d_state;        /* N: 16, 32, 64 or 128 */
+    int64_t n_groups;       /* G: divides H */
+} mss_ssd_dims;
+
+/*   x, y (M, H*P);  dt (M, H);  A_log (H);  B, C (M, G*N);
+ *   D_vec, dt_bias (H), may be NULL (= 0);
+ *   h0, h_last (B, H, P, N), may be NULL (h0 = 0 / not written).
+ * A sequence of length 0 still defines h_last (= h0, or zeros).          */
+int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, const float* A_log,
+                 const float* B, const float* C, const float* D_vec, const float* dt_bias,
+                 const float* h0, float* y, float* h_last, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mss_strerror(int status);
 

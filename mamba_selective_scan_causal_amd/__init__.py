@@ -58,9 +58,22 @@ def make_strides(x, z, delta, B, C, y) -> Strides:
     return Strides(ctypes.sizeof(Strides), 0, x, z, delta, B, C, y)
 
 
+class SsdDims(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("n_groups", ctypes.c_int64)]
+
+
+def make_ssd_dims(batch, seq_len, n_heads, head_dim, d_state, n_groups=1) -> SsdDims:
+    return SsdDims(ctypes.sizeof(SsdDims), 0, batch, seq_len, n_heads, head_dim, d_state,
+                   n_groups)
+
+
 EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_selective_step",
            "mss_selective_scan_strided", "mss_mamba1_core_strided",
            "mss_workspace_bytes", "mss_selective_scan_backward", "mss_conv1d_silu_backward",
+           "mss_ssd_scan",
            "mss_strerror", "mss_version", "mss_last_hip_error")
 
 OP_SELECTIVE_SCAN_BACKWARD = 1
@@ -90,10 +103,12 @@ def lib():
         L.mss_workspace_bytes.argtypes = [dp, i, ctypes.POINTER(sz)]
         L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
         L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
+        L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims)] + [p] * 11
         for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
                   "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
                   "mss_workspace_bytes", "mss_selective_scan_backward",
-                  "mss_conv1d_silu_backward", "mss_version", "mss_last_hip_error"):
+                  "mss_conv1d_silu_backward", "mss_ssd_scan", "mss_version",
+                  "mss_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         L.mss_strerror.argtypes = [ctypes.c_int]
         L.mss_strerror.restype = ctypes.c_char_p
@@ -357,3 +372,23 @@ def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, workspace=Non
         _ptr(b_conv, "b_conv", (D,), False), _ptr(du, "du", (M, D)), _ptr(dx, "dx", (M, D)),
         _ptr(dw, "dw_conv", (D, K)), _ptr(db, "db_conv", (D,)), wp, wn, _stream(stream)))
     return dx, dw, db
+
+
+def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, seq_len,
+             head_dim, d_state, n_groups=1, h_last=False, out=None, stream=None):
+    """Mamba-2 SSD scan: y (batch*seq_len, H*head_dim) and, when ``h_last`` is
+    True (or a tensor), the final state (batch, H, head_dim, d_state)."""
+    H = A_log.shape[0]
+    P, N, G = head_dim, d_state, n_groups
+    M = batch * seq_len
+    y = out if out is not None else _empty((M, H * P), x)
+    hl = (h_last if not isinstance(h_last, bool) else
+          (_empty((batch, H, P, N), x) if h_last else None))
+    dims = make_ssd_dims(batch, seq_len, H, P, N, G)
+    _check("mss_ssd_scan", lib().mss_ssd_scan(
+        ctypes.byref(dims), _ptr(x, "x", (M, H * P)), _ptr(dt, "dt", (M, H)),
+        _ptr(A_log, "A_log", (H,)), _ptr(B, "B", (M, G * N)), _ptr(C, "C", (M, G * N)),
+        _ptr(D_vec, "D_vec", (H,), False), _ptr(dt_bias, "dt_bias", (H,), False),
+        _ptr(h0, "h0", (batch, H, P, N), False), _ptr(y, "y", (M, H * P)),
+        _ptr(hl, "h_last", (batch, H, P, N), False), _stream(stream)))
+    return y, hl

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmss.so")
 
 SOURCES = ["mss_api.hip", "scan_kernel.hip", "conv_kernel.hip", "step_kernel.hip",
-           "scan_bwd_kernel.hip", "conv_bwd_kernel.hip"]
+           "scan_bwd_kernel.hip", "conv_bwd_kernel.hip", "ssd_kernel.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -15,6 +15,7 @@
 
 #include "launch.h"
 #include "launch_bwd.h"
+#include "launch_ssd.h"
 #include "mss.h"
 
 namespace {
@@ -542,6 +543,61 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
     const mss::StepArgs a{disc, Bt, D, static_cast<int>(N), static_cast<int>(K), x, z, delta,
                           A_log, B, C, D_vec, w_conv, b_conv, conv_state, h, y};
     const hipError_t e = mss::launch_step(a, stream);
+    return e == hipSuccess ? MSS_OK : hip_fail(e);
+}
+
+int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, const float* A_log,
+                 const float* B, const float* C, const float* D_vec, const float* dt_bias,
+                 const float* h0, float* y, float* h_last, hipStream_t stream) {
+    if (!dims || dims->struct_size != static_cast<int32_t>(sizeof(mss_ssd_dims)) ||
+        dims->reserved != 0)
+        return MSS_EINVAL;
+    const int64_t Bt = dims->batch, L = dims->seq_len, H = dims->n_heads, P = dims->head_dim;
+    const int64_t N = dims->d_state, G = dims->n_groups;
+    if (Bt < 0 || L < 0 || H < 1 || G < 1 || H % G != 0 || !mss::ssd_supported(P, N))
+        return MSS_EINVAL;
+    int64_t M, MHP, MH, MGN, BHPN;
+    if (!count(M, {Bt, L}) || !count(MHP, {Bt, L, H, P}) || !count(MH, {Bt, L, H}) ||
+        !count(MGN, {Bt, L, G, N}) || !count(BHPN, {Bt, H, P, N}))
+        return MSS_EINVAL;
+    Checker ck;
+    ck.in(x, MHP, true);
+    ck.in(dt, MH, true);
+    ck.in(A_log, H, true);
+    ck.in(B, MGN, true);
+    ck.in(C, MGN, true);
+    ck.in(D_vec, H, false);
+    ck.in(dt_bias, H, false);
+    ck.in(h0, BHPN, false);
+    ck.out(y, MHP, true);
+    ck.out(h_last, BHPN, false);
+    int st = ck.finish();
+    if (st != MSS_OK) return st;
+    if (Bt == 0) return MSS_OK;
+    if (L == 0) {
+        if (!h_last) return MSS_OK;
+        const hipError_t e = mss::launch_state_init(h0, h_last, BHPN, stream);
+        return e == hipSuccess ? MSS_OK : hip_fail(e);
+    }
+    // Segments: about four workgroups per CU, none shorter than
+    // MSS_SSD_MIN_SEG steps (default 512), so that the replay that rebuilds a
+    // segment's initial state stays a small share of its work.
+    static const int64_t wg_per_cu = env_or("MSS_SSD_WG_PER_CU", 4);
+    static const int64_t min_seg = env_or("MSS_SSD_MIN_SEG", 512);
+    const int64_t Q = mss::ssd_chunk_len();
+    const int64_t nchunks = (L + Q - 1) / Q;
+    const int64_t bh = Bt * H;
+    int64_t nseg = (cu_count() * wg_per_cu) / bh;
+    const int64_t min_chunks = (min_seg + Q - 1) / Q;
+    const int64_t max_seg = (nchunks + min_chunks - 1) / min_chunks;
+    if (nseg > max_seg) nseg = max_seg;
+    if (nseg < 1) nseg = 1;
+    const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
+    nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+    if (bh * nseg > INT32_MAX) return MSS_EINVAL;
+    const mss::SsdArgs a{Bt, L, H, P, N, G, nseg, seg_chunks, x, dt, A_log, B, C,
+                         D_vec, dt_bias, h0, y, h_last};
+    const hipError_t e = mss::launch_ssd(a, stream);
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 

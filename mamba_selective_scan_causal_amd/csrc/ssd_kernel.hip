@@ -1,0 +1,388 @@
+// ssd_kernel.hip -- Mamba-2 state-space-dual (SSD) scan for gfx950 on the
+// matrix cores.
+//
+// The recurrence the pages' Mamba2Block dispatches as ssd_chunk_forward
+// (builderforce-memory-engine 2026.7.14 -> 2026.9.28, src/model/mamba2_block.ts:
+// x (M, H*P), dt (M, H), B and C (M, G*N) split from the projections): per
+// batch row and head h (group g = h / (H/G)), with A_h = -exp(clamp(A_log_h))
+// and dv_t = softplus(dt_t + dt_bias_h),
+//   S_t = exp(dv_t A_h) S_{t-1} + dv_t x_t B_t^T      (S is P x N)
+//   y_t = S_t C_t + D_h x_t
+//
+// Chunked form.  Over a chunk of Q steps with c_i = sum_{r<=i} dv_r A_h:
+//   Y    = (L o C B^T) X  +  diag(e^{c}) C S_in^T...  (per head, P columns)
+//   with L_ij = e^{c_i - c_j} dv_j for i >= j (else 0), and
+//   S_out = e^{c_{Q-1}} S_in + sum_j e^{c_{Q-1} - c_j} dv_j x_j B_j^T.
+// Every product is a dense contraction: v_mfma_f32_16x16x4f32 (fp32 in, fp32
+// accumulate).  Indexing the summation as k = 4 (lane / 16) + step makes the
+// accumulator layout of an S tile (rows n, columns p: lane l holds
+// S[4 (l/16) + i][l % 16]) exactly the B operand of C S, so the state never
+// leaves the registers between chunks.
+//
+// Mapping.  One workgroup (4 waves) per (batch row, head, time segment).
+// Wave w owns the P columns [16 w c, ...) of S and of y.  Per chunk: the
+// chunk's X (transposed), B (both layouts), C and the decay prefix go to LDS;
+// three waves form the three nonzero 16 x 16 tiles of L o C B^T; each wave
+// then forms its y columns and updates its S columns.  A segment that starts
+// at t0 > 0 first rebuilds S(t0 - 1) by replaying the state update from the
+// point where every contribution before it has decayed by 2^-30 (for a
+// scalar-decay head this walk is exact and uniform), as the Mamba-1 kernels do.
+#include "device_math.h"
+#include "launch_ssd.h"
+
+namespace mss {
+namespace {
+
+constexpr int kQ = 32;            // steps per chunk
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kCut = 30.0f;     // replay until the carried part decays by 2^-30
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int P, int N>
+struct Cfg {
+    static constexpr int CT = P / 16;                   // column tiles of P
+    static constexpr int CTW = CT >= kWaves ? CT / kWaves : 1;   // per wave
+    static constexpr int NT = N / 16;
+    static constexpr int LDN = N + 4;                   // C, B rows (floats)
+    static constexpr int LDQ = kQ + 4;                  // Bt, Xt, G rows
+    // LDS layout (floats)
+    static constexpr int oC = 0;
+    static constexpr int oB = oC + kQ * LDN;
+    static constexpr int oBt = oB + kQ * LDN;
+    static constexpr int oXt = oBt + N * LDQ;
+    static constexpr int oG = oXt + P * LDQ;
+    static constexpr int oCum = oG + kQ * LDQ;
+    static constexpr int oDv = oCum + kQ;
+    static constexpr int oW = oDv + kQ;
+    static constexpr int oMisc = oW + kQ;
+    static constexpr int total = oMisc + 4;
+};
+
+template <int P, int N>
+struct Ssd {
+    using C_ = Cfg<P, N>;
+    const SsdArgs& a;
+    const int64_t b, h, g;
+    float* lds;
+    const float A2;        // A_h log2(e)
+    const float bias, dskip;
+    const uint32_t lane, wave, q16, g4;   // lane, wave, lane % 16, lane / 16
+
+    __device__ Ssd(const SsdArgs& a_, int64_t b_, int64_t h_, float* lds_)
+        : a(a_), b(b_), h(h_), g(h_ / (a_.H / a_.G)), lds(lds_),
+          A2(a_cont(a_.A_log[h_]) * kLog2e), bias(a_.dt_bias ? a_.dt_bias[h_] : 0.0f),
+          dskip(a_.D_vec ? a_.D_vec[h_] : 0.0f), lane(threadIdx.x & 63u),
+          wave(threadIdx.x >> 6), q16(threadIdx.x & 15u), g4((threadIdx.x & 63u) >> 4) {}
+
+    __device__ __forceinline__ int64_t row(int64_t t) const { return b * a.L + t; }
+
+    // Chunk [t0, t0 + kQ) into LDS (zeros past the sequence end, where dv = 0
+    // leaves S unchanged and no output is written).  FULL: also C.
+    template <bool FULL>
+    __device__ __forceinline__ void load_chunk(int64_t t0) const {
+        const int tid = threadIdx.x;
+        const int64_t HP = a.H * P, GN = a.G * N;
+        // X: kQ rows of P floats, stored transposed Xt[p][j]
+        for (int i = tid; i < kQ * (P / 4); i += kThreads) {
+            const int j = i / (P / 4), p4 = (i % (P / 4)) * 4;
+            const int64_t t = t0 + j;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < a.L) v = *reinterpret_cast<const float4*>(a.x + row(t) * HP + h * P + p4);
+            float* xt = lds + C_::oXt;
+            xt[(p4 + 0) * C_::LDQ + j] = v.x;
+            xt[(p4 + 1) * C_::LDQ + j] = v.y;
+            xt[(p4 + 2) * C_::LDQ + j] = v.z;
+            xt[(p4 + 3) * C_::LDQ + j] = v.w;
+        }
+        // B (both layouts) and C: kQ rows of N floats
+        for (int i = tid; i < kQ * (N / 4); i += kThreads) {
+            const int j = i / (N / 4), n4 = (i % (N / 4)) * 4;
+            const int64_t t = t0 + j;
+            float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+            if (t < a.L) {
+                vb = *reinterpret_cast<const float4*>(a.Bm + row(t) * GN + g * N + n4);
+                if constexpr (FULL)
+                    vc = *reinterpret_cast<const float4*>(a.Cm + row(t) * GN + g * N + n4);
+            }
+            *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = vb;
+            float* bt = lds + C_::oBt;
+            bt[(n4 + 0) * C_::LDQ + j] = vb.x;
+            bt[(n4 + 1) * C_::LDQ + j] = vb.y;
+            bt[(n4 + 2) * C_::LDQ + j] = vb.z;
+            bt[(n4 + 3) * C_::LDQ + j] = vb.w;
+            if constexpr (FULL) *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = vc;
+        }
+        // dv, the decay prefix c (log2 units) and the state weights
+        if (tid < kQ) {
+            const int64_t t = t0 + tid;
+            const float dv = t < a.L ? softplus(a.dt[row(t) * a.H + h] + bias) : 0.0f;
+            float c = dv * A2;
+#pragma unroll
+            for (int o = 1; o < kQ; o <<= 1) {
+                const float v = __shfl_up(c, o, kQ);
+                if (tid >= o) c += v;
+            }
+            const float last = __shfl(c, kQ - 1, kQ);
+            lds[C_::oCum + tid] = c;
+            lds[C_::oDv + tid] = dv;
+            lds[C_::oW + tid] = ex2(last - c) * dv;
+        }
+        __syncthreads();
+    }
+
+    // L o C B^T: the three nonzero 16 x 16 tiles (waves 0-2); wave 3 writes
+    // the zero tile above the diagonal.
+    __device__ __forceinline__ void form_g() const {
+        const float* cum = lds + C_::oCum;
+        const float* dvs = lds + C_::oDv;
+        float* G = lds + C_::oG;
+        if (wave == 3) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) G[(4 * g4 + i) * C_::LDQ + 16 + q16] = 0.0f;
+            return;
+        }
+        const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        const float* Cr = lds + C_::oC + (16 * ti + q16) * C_::LDN + 4 * g4;
+        const float* Br = lds + C_::oB + (16 * tj + q16) * C_::LDN + 4 * g4;
+#pragma unroll
+        for (int kt = 0; kt < C_::NT; kt++) {
+            const float4 ca = *reinterpret_cast<const float4*>(Cr + 16 * kt);
+            const float4 bb = *reinterpret_cast<const float4*>(Br + 16 * kt);
+            acc = mfma(ca.x, bb.x, acc);
+            acc = mfma(ca.y, bb.y, acc);
+            acc = mfma(ca.z, bb.z, acc);
+            acc = mfma(ca.w, bb.w, acc);
+        }
+        const int j = 16 * tj + q16;
+        const float cj = cum[j], dj = dvs[j];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int i = 16 * ti + 4 * g4 + r;
+            G[i * C_::LDQ + j] = i >= j ? acc[r] * ex2(cum[i] - cj) * dj : 0.0f;
+        }
+    }
+
+    // y for the chunk (rows < nout are written) from G X + (e^c C) S + D x.
+    __device__ __forceinline__ void output(const v4f (&S)[C_::CTW][C_::NT], int64_t t0,
+                                           int nout) const {
+        const float* G = lds + C_::oG;
+        const float* Xt = lds + C_::oXt;
+        const float* Cc = lds + C_::oC;
+        const float* cum = lds + C_::oCum;
+        const int64_t HP = a.H * P;
+#pragma unroll
+        for (int c = 0; c < C_::CTW; c++) {
+            const int ct = wave * C_::CTW + c;
+            if (ct >= C_::CT) break;
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++) {
+                v4f y = {0.f, 0.f, 0.f, 0.f};
+                const float* Gr = G + (16 * rt + q16) * C_::LDQ + 4 * g4;
+                const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
+#pragma unroll
+                for (int kt = 0; kt < kQ / 16; kt++) {
+                    const float4 ga = *reinterpret_cast<const float4*>(Gr + 16 * kt);
+                    const float4 xb = *reinterpret_cast<const float4*>(Xr + 16 * kt);
+                    y = mfma(ga.x, xb.x, y);
+                    y = mfma(ga.y, xb.y, y);
+                    y = mfma(ga.z, xb.z, y);
+                    y = mfma(ga.w, xb.w, y);
+                }
+                const float f = ex2(cum[16 * rt + q16]);
+                const float* Cr = Cc + (16 * rt + q16) * C_::LDN + 4 * g4;
+#pragma unroll
+                for (int tn = 0; tn < C_::NT; tn++) {
+                    const float4 ca = *reinterpret_cast<const float4*>(Cr + 16 * tn);
+                    y = mfma(ca.x * f, S[c][tn][0], y);
+                    y = mfma(ca.y * f, S[c][tn][1], y);
+                    y = mfma(ca.z * f, S[c][tn][2], y);
+                    y = mfma(ca.w * f, S[c][tn][3], y);
+                }
+                const int p = 16 * ct + q16;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int i = 16 * rt + 4 * g4 + r;
+                    if (i < nout)
+                        a.y[row(t0 + i) * HP + h * P + p] =
+                            __builtin_fmaf(dskip, Xt[p * C_::LDQ + i], y[r]);
+                }
+            }
+        }
+    }
+
+    // S <- e^{c_{Q-1}} S + sum_j w_j B_j^T x_j (this wave's columns).
+    __device__ __forceinline__ void update(v4f (&S)[C_::CTW][C_::NT]) const {
+        const float decay = ex2(lds[C_::oCum + kQ - 1]);
+        const float* Bt = lds + C_::oBt;
+        const float* Xt = lds + C_::oXt;
+        const float* w = lds + C_::oW;
+#pragma unroll
+        for (int c = 0; c < C_::CTW; c++) {
+            const int ct = wave * C_::CTW + c;
+            if (ct >= C_::CT) break;
+            const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
+            float4 xb[kQ / 16], wv[kQ / 16];
+#pragma unroll
+            for (int kt = 0; kt < kQ / 16; kt++) {
+                xb[kt] = *reinterpret_cast<const float4*>(Xr + 16 * kt);
+                wv[kt] = *reinterpret_cast<const float4*>(w + 16 * kt + 4 * g4);
+            }
+#pragma unroll
+            for (int tn = 0; tn < C_::NT; tn++) {
+                v4f s = S[c][tn] * decay;
+                const float* Br = Bt + (16 * tn + q16) * C_::LDQ + 4 * g4;
+#pragma unroll
+                for (int kt = 0; kt < kQ / 16; kt++) {
+                    const float4 ba = *reinterpret_cast<const float4*>(Br + 16 * kt);
+                    s = mfma(ba.x * wv[kt].x, xb[kt].x, s);
+                    s = mfma(ba.y * wv[kt].y, xb[kt].y, s);
+                    s = mfma(ba.z * wv[kt].z, xb[kt].z, s);
+                    s = mfma(ba.w * wv[kt].w, xb[kt].w, s);
+                }
+                S[c][tn] = s;
+            }
+        }
+    }
+
+    // First step of the replay that rebuilds S(t0 - 1): walk dt backwards
+    // until sum dv |A| >= 30 ln 2 (every contribution before it has decayed
+    // by 2^-30), or t = 0.  One wave walks 64 steps at a time.
+    __device__ __forceinline__ int64_t replay_start(int64_t t0) const {
+        if (t0 == 0) return 0;
+        int64_t* res = reinterpret_cast<int64_t*>(lds + C_::oMisc);
+        if (wave == 0) {
+            float total = 0.0f;
+            int64_t t = t0;
+            int64_t found = 0;
+            while (t > 0) {
+                const int64_t tt = t - 1 - static_cast<int64_t>(lane);   // lane 0 = newest
+                const float dv = tt >= 0 ? softplus(a.dt[row(tt) * a.H + h] + bias) : 0.0f;
+                float s = dv * -A2;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const float v = __shfl_up(s, o);
+                    if (lane >= static_cast<uint32_t>(o)) s += v;
+                }
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(tt >= 0 && total + s >= kCut);
+                if (hit) {
+                    found = t - 1 - static_cast<int64_t>(__builtin_ctzll(hit));
+                    break;
+                }
+                total += __shfl(s, kWave - 1);
+                t -= kWave;
+            }
+            if (lane == 0) *res = found > 0 ? found : 0;
+        }
+        __syncthreads();
+        const int64_t r = *res;
+        __syncthreads();
+        return r;
+    }
+};
+
+template <int P, int N>
+__global__ __launch_bounds__(kThreads) void ssd_kernel(SsdArgs a) {
+    using C_ = Cfg<P, N>;
+    __shared__ __align__(16) float lds[C_::total];
+    const int64_t wg = blockIdx.x;
+    const int64_t bh = wg / a.nseg;
+    const int64_t sg = wg - bh * a.nseg;
+    const int64_t b = bh / a.H, h = bh - b * a.H;
+    const int64_t nchunks = (a.L + kQ - 1) / kQ;
+    const int64_t c0 = sg * a.seg_chunks;
+    const int64_t c1 = c0 + a.seg_chunks < nchunks ? c0 + a.seg_chunks : nchunks;
+    Ssd<P, N> sd(a, b, h, lds);
+
+    v4f S[C_::CTW][C_::NT];
+    const int64_t tw = sd.replay_start(c0 * kQ);
+    const int64_t cw = tw / kQ;
+#pragma unroll
+    for (int c = 0; c < C_::CTW; c++) {
+        const int ct = sd.wave * C_::CTW + c;
+#pragma unroll
+        for (int tn = 0; tn < C_::NT; tn++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int n = 16 * tn + 4 * sd.g4 + r, p = 16 * ct + sd.q16;
+                S[c][tn][r] = (cw == 0 && a.h0 && ct < C_::CT)
+                                  ? a.h0[((b * a.H + h) * P + p) * N + n]
+                                  : 0.0f;
+            }
+    }
+    for (int64_t c = cw; c < c0; c++) {          // state-only replay
+        sd.template load_chunk<false>(c * kQ);
+        sd.update(S);
+        __syncthreads();
+    }
+    for (int64_t c = c0; c < c1; c++) {
+        const int64_t t0 = c * kQ;
+        sd.template load_chunk<true>(t0);
+        sd.form_g();
+        __syncthreads();
+        const int nout = a.L - t0 < kQ ? static_cast<int>(a.L - t0) : kQ;
+        sd.output(S, t0, nout);
+        sd.update(S);
+        __syncthreads();
+    }
+    if (c1 == nchunks && a.h_last) {
+#pragma unroll
+        for (int c = 0; c < C_::CTW; c++) {
+            const int ct = sd.wave * C_::CTW + c;
+            if (ct >= C_::CT) break;
+#pragma unroll
+            for (int tn = 0; tn < C_::NT; tn++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int n = 16 * tn + 4 * sd.g4 + r, p = 16 * ct + sd.q16;
+                    a.h_last[((b * a.H + h) * P + p) * N + n] = S[c][tn][r];
+                }
+        }
+    }
+}
+
+template <int P, int N>
+hipError_t launch_pn(const SsdArgs& a, hipStream_t st) {
+    const int64_t nwg = a.B * a.H * a.nseg;
+    hipLaunchKernelGGL((ssd_kernel<P, N>), dim3(static_cast<unsigned>(nwg)), dim3(kThreads), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_p(const SsdArgs& a, hipStream_t st) {
+    switch (a.N) {
+        case 16: return launch_pn<P, 16>(a, st);
+        case 32: return launch_pn<P, 32>(a, st);
+        case 64: return launch_pn<P, 64>(a, st);
+        case 128: return launch_pn<P, 128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool ssd_supported(int64_t P, int64_t N) {
+    return (P == 16 || P == 32 || P == 64 || P == 128) &&
+           (N == 16 || N == 32 || N == 64 || N == 128);
+}
+
+int ssd_chunk_len() { return kQ; }
+
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t st) {
+    switch (a.P) {
+        case 16: return launch_p<16>(a, st);
+        case 32: return launch_p<32>(a, st);
+        case 64: return launch_p<64>(a, st);
+        case 128: return launch_p<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mss

@@ -272,3 +272,28 @@ def test_conv_backward_validation(L):
     assert conv_bwd_call(L, d, ws=None) == EWORKSPACE
     assert conv_bwd_call(L, d, ws_size=1) == EWORKSPACE
     assert conv_bwd_call(L, d, du=ctypes.c_void_p(BASE + 4 * (1 << 32) + 8)) == EALIGN
+
+
+def ssd_call(L, dims, **over):
+    args = dict(x=fake(1), dt=fake(2), A_log=fake(3), B=fake(4), C=fake(5), D=fake(6),
+                bias=fake(7), h0=None, y=fake(8), h_last=None)
+    args.update(over)
+    return L.mss_ssd_scan(ctypes.byref(dims) if dims is not None else None, *args.values(), None)
+
+
+def test_ssd_validation(L):
+    d = mss.make_ssd_dims(2, 64, 8, 64, 128, 2)
+    assert ssd_call(L, None) == EINVAL
+    bad = mss.make_ssd_dims(2, 64, 8, 64, 128, 2)
+    bad.struct_size = 48
+    assert ssd_call(L, bad) == EINVAL
+    assert ssd_call(L, mss.make_ssd_dims(2, 64, 8, 48, 128)) == EINVAL     # head_dim
+    assert ssd_call(L, mss.make_ssd_dims(2, 64, 8, 64, 96)) == EINVAL      # d_state
+    assert ssd_call(L, mss.make_ssd_dims(2, 64, 8, 64, 128, 3)) == EINVAL  # G does not divide H
+    assert ssd_call(L, mss.make_ssd_dims(2, 64, 0, 64, 128)) == EINVAL
+    for name in ("x", "dt", "A_log", "B", "C", "y"):
+        assert ssd_call(L, d, **{name: None}) == EINVAL, name
+    assert ssd_call(L, d, y=fake(1)) == EALIAS
+    assert ssd_call(L, d, x=ctypes.c_void_p(BASE + (1 << 32) + 8)) == EALIGN
+    assert ssd_call(L, mss.make_ssd_dims(0, 64, 8, 64, 128, 2)) == 0        # empty: nothing to do
+    assert ctypes.sizeof(mss.SsdDims) == 56
