@@ -125,6 +125,7 @@ def extras(w, d, y, disc, stream):
 
     t64 = _time_ms(decode64, stream, 3, warm=1)
     res["backward"] = backward_extras(w, d, stream)
+    res["ssd"] = ssd_extras(stream)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
     step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
@@ -173,6 +174,42 @@ def backward_extras(w, d, stream, reps=5):
             "total_ms": t_sb + t_cb}
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3          # MI355X dense fp32 matrix, AMD published
+SSD_CHUNK = 32
+
+
+def ssd_flops(w) -> int:
+    """Dense work of the chunked SSD form with the causal half of the two
+    quadratic terms: per (step, head) Q N / 2 + Q P / 2 multiply-adds for
+    (C B^T) and (L o C B^T) X, and N P each for C S and the state update."""
+    Q, N, P = SSD_CHUNK, w.d_state, w.head_dim
+    return 2 * w.M * w.n_heads * (Q * N // 2 + Q * P // 2 + 2 * N * P)
+
+
+def ssd_extras(stream, reps=5):
+    """The Mamba-2 SSD scan (mss_ssd_scan) on B4 L8192 H80 P64 N128 G1."""
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+    w = gen.SSD_2P7B
+    inp = gen.generate_ssd(w)
+    d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    y = torch.empty((w.M, w.n_heads * w.head_dim), device="cuda")
+    t = _time_ms(lambda: mss.ssd_scan(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D_vec"],
+                                      d["dt_bias"], None, batch=w.batch, seq_len=w.seq_len,
+                                      head_dim=w.head_dim, d_state=w.d_state,
+                                      n_groups=w.n_groups, out=y, stream=stream),
+                 stream, reps)
+    fl = ssd_flops(w)
+    bytes_ = 4 * (2 * w.M * w.n_heads * w.head_dim + w.M * w.n_heads
+                  + 2 * w.M * w.n_groups * w.d_state)
+    tf = fl / t / 1e9
+    return {"workload": w.name, "ms": t, "algorithmic_flops": fl, "TFLOPs": tf,
+            "frac_of_fp32_mfma_peak": tf / MFMA_F32_PEAK_TFLOPS,
+            "algorithmic_bytes": bytes_, "GBps": bytes_ / t / 1e6,
+            "tokens_per_s": w.M / (t / 1e3)}
+
+
 def cpu_baseline(w, inp, disc, target_s=15.0):
     """The oracle as it stands, on a bounded sample of whole (b, d) columns of
     the same workload, on all host cores it may use."""
@@ -211,9 +248,9 @@ def main():
                     help="skip the side measurements (other mode, unfused path, decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--part", default="all", choices=("all", "backward"),
-                    help="backward: only the backward passes on the same workload "
-                         "(one JSON line of their timings, for profiling)")
+    ap.add_argument("--part", default="all", choices=("all", "backward", "ssd"),
+                    help="backward: only the backward passes on the same workload; ssd: only "
+                         "the Mamba-2 SSD scan (one JSON line of timings, for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
@@ -231,6 +268,9 @@ def main():
     w = gen.MAMBA_2P8B
     inp = gen.generate(w)
     d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    if args.part == "ssd":
+        print(json.dumps(ssd_extras(torch.cuda.current_stream(), reps=max(args.steps, 1))))
+        return
     if args.part == "backward":
         res = backward_extras(w, d, torch.cuda.current_stream(), reps=max(args.steps, 1))
         res["workload"] = w.name

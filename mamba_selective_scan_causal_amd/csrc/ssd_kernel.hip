@@ -82,46 +82,83 @@ struct Ssd {
 
     __device__ __forceinline__ int64_t row(int64_t t) const { return b * a.L + t; }
 
-    // Chunk [t0, t0 + kQ) into LDS (zeros past the sequence end, where dv = 0
-    // leaves S unchanged and no output is written).  FULL: also C.
-    template <bool FULL>
-    __device__ __forceinline__ void load_chunk(int64_t t0) const {
+    // The chunk's global data, held in registers between the load (issued
+    // one chunk ahead) and the write to LDS.
+    static constexpr int kXv = (kQ * (P / 4) + kThreads - 1) / kThreads;   // float4 per thread
+    static constexpr int kBv = (kQ * (N / 4) + kThreads - 1) / kThreads;
+    struct Stage {
+        float4 xv[kXv], bv[kBv], cv[kBv];
+        float dt;
+    };
+
+    // Loads of chunk [t0, t0 + kQ) (zeros past the sequence end, where dv = 0
+    // leaves S unchanged and no output is written).  full: also C.
+    __device__ __forceinline__ void issue(Stage& st, int64_t t0, bool full) const {
         const int tid = threadIdx.x;
         const int64_t HP = a.H * P, GN = a.G * N;
-        // X: kQ rows of P floats, stored transposed Xt[p][j]
-        for (int i = tid; i < kQ * (P / 4); i += kThreads) {
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kXv; k++) {
+            const int i = tid + k * kThreads;
             const int j = i / (P / 4), p4 = (i % (P / 4)) * 4;
             const int64_t t = t0 + j;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < a.L) v = *reinterpret_cast<const float4*>(a.x + row(t) * HP + h * P + p4);
-            float* xt = lds + C_::oXt;
-            xt[(p4 + 0) * C_::LDQ + j] = v.x;
-            xt[(p4 + 1) * C_::LDQ + j] = v.y;
-            xt[(p4 + 2) * C_::LDQ + j] = v.z;
-            xt[(p4 + 3) * C_::LDQ + j] = v.w;
+            float4 v = z4;
+            if (i < kQ * (P / 4) && t < a.L)
+                v = *reinterpret_cast<const float4*>(a.x + row(t) * HP + h * P + p4);
+            st.xv[k] = v;
         }
-        // B (both layouts) and C: kQ rows of N floats
-        for (int i = tid; i < kQ * (N / 4); i += kThreads) {
+#pragma unroll
+        for (int k = 0; k < kBv; k++) {
+            const int i = tid + k * kThreads;
             const int j = i / (N / 4), n4 = (i % (N / 4)) * 4;
             const int64_t t = t0 + j;
-            float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
-            if (t < a.L) {
-                vb = *reinterpret_cast<const float4*>(a.Bm + row(t) * GN + g * N + n4);
-                if constexpr (FULL)
-                    vc = *reinterpret_cast<const float4*>(a.Cm + row(t) * GN + g * N + n4);
+            const bool ok = i < kQ * (N / 4) && t < a.L;
+            const int64_t o = row(ok ? t : 0) * GN + g * N + n4;
+            float4 vb = z4, vc = z4;
+            if (ok) {
+                vb = *reinterpret_cast<const float4*>(a.Bm + o);
+                if (full) vc = *reinterpret_cast<const float4*>(a.Cm + o);
             }
-            *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = vb;
-            float* bt = lds + C_::oBt;
-            bt[(n4 + 0) * C_::LDQ + j] = vb.x;
-            bt[(n4 + 1) * C_::LDQ + j] = vb.y;
-            bt[(n4 + 2) * C_::LDQ + j] = vb.z;
-            bt[(n4 + 3) * C_::LDQ + j] = vb.w;
-            if constexpr (FULL) *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = vc;
+            st.bv[k] = vb;
+            st.cv[k] = vc;
         }
-        // dv, the decay prefix c (log2 units) and the state weights
+        const int64_t t = t0 + tid;
+        float dtv = 0.0f;
+        if (tid < kQ && t < a.L) dtv = a.dt[row(t) * a.H + h];
+        st.dt = dtv;
+    }
+
+    // Staged chunk into LDS: Xt (transposed), B, Bt, C, and dv, the decay
+    // prefix c (log2 units) and the state weights.  Ends with a barrier.
+    __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
+        const int tid = threadIdx.x;
+        float* xt = lds + C_::oXt;
+#pragma unroll
+        for (int k = 0; k < kXv; k++) {
+            const int i = tid + k * kThreads;
+            if (i >= kQ * (P / 4)) break;
+            const int j = i / (P / 4), p4 = (i % (P / 4)) * 4;
+            xt[(p4 + 0) * C_::LDQ + j] = st.xv[k].x;
+            xt[(p4 + 1) * C_::LDQ + j] = st.xv[k].y;
+            xt[(p4 + 2) * C_::LDQ + j] = st.xv[k].z;
+            xt[(p4 + 3) * C_::LDQ + j] = st.xv[k].w;
+        }
+        float* bt = lds + C_::oBt;
+#pragma unroll
+        for (int k = 0; k < kBv; k++) {
+            const int i = tid + k * kThreads;
+            if (i >= kQ * (N / 4)) break;
+            const int j = i / (N / 4), n4 = (i % (N / 4)) * 4;
+            *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = st.bv[k];
+            *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = st.cv[k];
+            bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x;
+            bt[(n4 + 1) * C_::LDQ + j] = st.bv[k].y;
+            bt[(n4 + 2) * C_::LDQ + j] = st.bv[k].z;
+            bt[(n4 + 3) * C_::LDQ + j] = st.bv[k].w;
+        }
         if (tid < kQ) {
             const int64_t t = t0 + tid;
-            const float dv = t < a.L ? softplus(a.dt[row(t) * a.H + h] + bias) : 0.0f;
+            const float dv = t < a.L ? softplus(st.dt + bias) : 0.0f;
             float c = dv * A2;
 #pragma unroll
             for (int o = 1; o < kQ; o <<= 1) {
@@ -316,18 +353,20 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SsdArgs a) {
                                   : 0.0f;
             }
     }
-    for (int64_t c = cw; c < c0; c++) {          // state-only replay
-        sd.template load_chunk<false>(c * kQ);
-        sd.update(S);
-        __syncthreads();
-    }
-    for (int64_t c = c0; c < c1; c++) {
+    // Chunks [cw, c0) rebuild the state only; [c0, c1) also produce y.  The
+    // loads of chunk c + 1 are in flight while chunk c computes.
+    typename Ssd<P, N>::Stage st;
+    sd.issue(st, cw * kQ, cw >= c0);
+    for (int64_t c = cw; c < c1; c++) {
         const int64_t t0 = c * kQ;
-        sd.template load_chunk<true>(t0);
-        sd.form_g();
-        __syncthreads();
-        const int nout = a.L - t0 < kQ ? static_cast<int>(a.L - t0) : kQ;
-        sd.output(S, t0, nout);
+        sd.commit(st, t0);
+        if (c + 1 < c1) sd.issue(st, t0 + kQ, c + 1 >= c0);
+        if (c >= c0) {
+            sd.form_g();
+            __syncthreads();
+            const int nout = a.L - t0 < kQ ? static_cast<int>(a.L - t0) : kQ;
+            sd.output(S, t0, nout);
+        }
         sd.update(S);
         __syncthreads();
     }
