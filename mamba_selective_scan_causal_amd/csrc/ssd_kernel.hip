@@ -83,7 +83,10 @@ struct Ssd {
     __device__ __forceinline__ int64_t row(int64_t t) const { return b * a.L + t; }
 
     // The chunk's global data, held in registers between the load (issued
-    // one chunk ahead) and the write to LDS.
+    // one chunk ahead) and the write to LDS.  Element idx of a tensor's chunk
+    // is step j = idx % kQ and column (idx / kQ) * 4: consecutive lanes take
+    // consecutive steps, so the transposed LDS writes (Xt, Bt) hit
+    // consecutive banks.
     static constexpr int kXv = (kQ * (P / 4) + kThreads - 1) / kThreads;   // float4 per thread
     static constexpr int kBv = (kQ * (N / 4) + kThreads - 1) / kThreads;
     struct Stage {
@@ -100,7 +103,7 @@ struct Ssd {
 #pragma unroll
         for (int k = 0; k < kXv; k++) {
             const int i = tid + k * kThreads;
-            const int j = i / (P / 4), p4 = (i % (P / 4)) * 4;
+            const int j = i % kQ, p4 = (i / kQ) * 4;
             const int64_t t = t0 + j;
             float4 v = z4;
             if (i < kQ * (P / 4) && t < a.L)
@@ -110,7 +113,7 @@ struct Ssd {
 #pragma unroll
         for (int k = 0; k < kBv; k++) {
             const int i = tid + k * kThreads;
-            const int j = i / (N / 4), n4 = (i % (N / 4)) * 4;
+            const int j = i % kQ, n4 = (i / kQ) * 4;
             const int64_t t = t0 + j;
             const bool ok = i < kQ * (N / 4) && t < a.L;
             const int64_t o = row(ok ? t : 0) * GN + g * N + n4;
@@ -137,7 +140,7 @@ struct Ssd {
         for (int k = 0; k < kXv; k++) {
             const int i = tid + k * kThreads;
             if (i >= kQ * (P / 4)) break;
-            const int j = i / (P / 4), p4 = (i % (P / 4)) * 4;
+            const int j = i % kQ, p4 = (i / kQ) * 4;
             xt[(p4 + 0) * C_::LDQ + j] = st.xv[k].x;
             xt[(p4 + 1) * C_::LDQ + j] = st.xv[k].y;
             xt[(p4 + 2) * C_::LDQ + j] = st.xv[k].z;
@@ -148,7 +151,7 @@ struct Ssd {
         for (int k = 0; k < kBv; k++) {
             const int i = tid + k * kThreads;
             if (i >= kQ * (N / 4)) break;
-            const int j = i / (N / 4), n4 = (i % (N / 4)) * 4;
+            const int j = i % kQ, n4 = (i / kQ) * 4;
             *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = st.bv[k];
             *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = st.cv[k];
             bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x;
@@ -185,7 +188,9 @@ struct Ssd {
             return;
         }
         const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        // two accumulators over alternating halves of each k tile, added at
+        // the end (independent chains for the matrix pipe)
+        v4f acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
         const float* Cr = lds + C_::oC + (16 * ti + q16) * C_::LDN + 4 * g4;
         const float* Br = lds + C_::oB + (16 * tj + q16) * C_::LDN + 4 * g4;
 #pragma unroll
@@ -193,10 +198,11 @@ struct Ssd {
             const float4 ca = *reinterpret_cast<const float4*>(Cr + 16 * kt);
             const float4 bb = *reinterpret_cast<const float4*>(Br + 16 * kt);
             acc = mfma(ca.x, bb.x, acc);
-            acc = mfma(ca.y, bb.y, acc);
+            acc2 = mfma(ca.y, bb.y, acc2);
             acc = mfma(ca.z, bb.z, acc);
-            acc = mfma(ca.w, bb.w, acc);
+            acc2 = mfma(ca.w, bb.w, acc2);
         }
+        acc += acc2;
         const int j = 16 * tj + q16;
         const float cj = cum[j], dj = dvs[j];
 #pragma unroll
@@ -207,6 +213,7 @@ struct Ssd {
     }
 
     // y for the chunk (rows < nout are written) from G X + (e^c C) S + D x.
+    // The two 16-row tiles run interleaved (independent accumulation chains).
     __device__ __forceinline__ void output(const v4f (&S)[C_::CTW][C_::NT], int64_t t0,
                                            int nout) const {
         const float* G = lds + C_::oG;
@@ -214,42 +221,54 @@ struct Ssd {
         const float* Cc = lds + C_::oC;
         const float* cum = lds + C_::oCum;
         const int64_t HP = a.H * P;
+        const float f0 = ex2(cum[q16]), f1 = ex2(cum[16 + q16]);
 #pragma unroll
         for (int c = 0; c < C_::CTW; c++) {
             const int ct = wave * C_::CTW + c;
             if (ct >= C_::CT) break;
+            v4f y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
+            const float* G0 = G + q16 * C_::LDQ + 4 * g4;
+            const float* G1 = G0 + 16 * C_::LDQ;
+            const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
 #pragma unroll
-            for (int rt = 0; rt < 2; rt++) {
-                v4f y = {0.f, 0.f, 0.f, 0.f};
-                const float* Gr = G + (16 * rt + q16) * C_::LDQ + 4 * g4;
-                const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
+            for (int kt = 0; kt < kQ / 16; kt++) {
+                const float4 xb = *reinterpret_cast<const float4*>(Xr + 16 * kt);
+                const float4 g0 = *reinterpret_cast<const float4*>(G0 + 16 * kt);
+                const float4 g1 = *reinterpret_cast<const float4*>(G1 + 16 * kt);
+                y0 = mfma(g0.x, xb.x, y0);
+                y1 = mfma(g1.x, xb.x, y1);
+                y0 = mfma(g0.y, xb.y, y0);
+                y1 = mfma(g1.y, xb.y, y1);
+                y0 = mfma(g0.z, xb.z, y0);
+                y1 = mfma(g1.z, xb.z, y1);
+                y0 = mfma(g0.w, xb.w, y0);
+                y1 = mfma(g1.w, xb.w, y1);
+            }
+            const float* C0 = Cc + q16 * C_::LDN + 4 * g4;
+            const float* C1 = C0 + 16 * C_::LDN;
 #pragma unroll
-                for (int kt = 0; kt < kQ / 16; kt++) {
-                    const float4 ga = *reinterpret_cast<const float4*>(Gr + 16 * kt);
-                    const float4 xb = *reinterpret_cast<const float4*>(Xr + 16 * kt);
-                    y = mfma(ga.x, xb.x, y);
-                    y = mfma(ga.y, xb.y, y);
-                    y = mfma(ga.z, xb.z, y);
-                    y = mfma(ga.w, xb.w, y);
-                }
-                const float f = ex2(cum[16 * rt + q16]);
-                const float* Cr = Cc + (16 * rt + q16) * C_::LDN + 4 * g4;
+            for (int tn = 0; tn < C_::NT; tn++) {
+                const float4 c0 = *reinterpret_cast<const float4*>(C0 + 16 * tn);
+                const float4 c1 = *reinterpret_cast<const float4*>(C1 + 16 * tn);
+                y0 = mfma(c0.x * f0, S[c][tn][0], y0);
+                y1 = mfma(c1.x * f1, S[c][tn][0], y1);
+                y0 = mfma(c0.y * f0, S[c][tn][1], y0);
+                y1 = mfma(c1.y * f1, S[c][tn][1], y1);
+                y0 = mfma(c0.z * f0, S[c][tn][2], y0);
+                y1 = mfma(c1.z * f1, S[c][tn][2], y1);
+                y0 = mfma(c0.w * f0, S[c][tn][3], y0);
+                y1 = mfma(c1.w * f1, S[c][tn][3], y1);
+            }
+            const int p = 16 * ct + q16;
 #pragma unroll
-                for (int tn = 0; tn < C_::NT; tn++) {
-                    const float4 ca = *reinterpret_cast<const float4*>(Cr + 16 * tn);
-                    y = mfma(ca.x * f, S[c][tn][0], y);
-                    y = mfma(ca.y * f, S[c][tn][1], y);
-                    y = mfma(ca.z * f, S[c][tn][2], y);
-                    y = mfma(ca.w * f, S[c][tn][3], y);
-                }
-                const int p = 16 * ct + q16;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int i = 16 * rt + 4 * g4 + r;
-                    if (i < nout)
-                        a.y[row(t0 + i) * HP + h * P + p] =
-                            __builtin_fmaf(dskip, Xt[p * C_::LDQ + i], y[r]);
-                }
+            for (int r = 0; r < 4; r++) {
+                const int i0 = 4 * g4 + r, i1 = 16 + 4 * g4 + r;
+                if (i0 < nout)
+                    a.y[row(t0 + i0) * HP + h * P + p] =
+                        __builtin_fmaf(dskip, Xt[p * C_::LDQ + i0], y0[r]);
+                if (i1 < nout)
+                    a.y[row(t0 + i1) * HP + h * P + p] =
+                        __builtin_fmaf(dskip, Xt[p * C_::LDQ + i1], y1[r]);
             }
         }
     }
