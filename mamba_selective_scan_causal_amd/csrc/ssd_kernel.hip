@@ -20,8 +20,9 @@
 // leaves the registers between chunks.
 //
 // Mapping.  One workgroup (4 waves) per (batch row, head, time segment).
-// Wave w owns the P columns [16 w c, ...) of S and of y.  Per chunk: the
-// chunk's X (transposed), B (both layouts), C and the decay prefix go to LDS;
+// Wave w owns the P columns [16 w c, ...) of S and of y.  Per chunk (its
+// loads issued one chunk ahead into registers): X (transposed), B, B^T
+// weighted by the state weights, C and the decay prefix go to LDS;
 // three waves form the three nonzero 16 x 16 tiles of L o C B^T; each wave
 // then forms its y columns and updates its S columns.  A segment that starts
 // at t0 > 0 first rebuilds S(t0 - 1) by replaying the state update from the
@@ -59,8 +60,7 @@ struct Cfg {
     static constexpr int oG = oXt + P * LDQ;
     static constexpr int oCum = oG + kQ * LDQ;
     static constexpr int oDv = oCum + kQ;
-    static constexpr int oW = oDv + kQ;
-    static constexpr int oMisc = oW + kQ;
+    static constexpr int oMisc = oDv + kQ;
     static constexpr int total = oMisc + 4;
 };
 
@@ -125,9 +125,10 @@ struct Ssd {
             st.bv[k] = vb;
             st.cv[k] = vc;
         }
-        const int64_t t = t0 + tid;
+        // every thread loads dt of its step (tid % kQ)
+        const int64_t t = t0 + (tid % kQ);
         float dtv = 0.0f;
-        if (tid < kQ && t < a.L) dtv = a.dt[row(t) * a.H + h];
+        if (t < a.L) dtv = a.dt[row(t) * a.H + h];
         st.dt = dtv;
     }
 
@@ -135,6 +136,23 @@ struct Ssd {
     // prefix c (log2 units) and the state weights.  Ends with a barrier.
     __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
         const int tid = threadIdx.x;
+        // dv, the decay prefix c (log2 units) and the state weight
+        // w_j = 2^{c_{Q-1} - c_j} dv_j of this thread's step j = tid % kQ,
+        // computed by every 32-lane half (shuffles of width kQ).
+        const int jj = tid % kQ;
+        const float dv = t0 + jj < a.L ? softplus(st.dt + bias) : 0.0f;
+        float cj = dv * A2;
+#pragma unroll
+        for (int o = 1; o < kQ; o <<= 1) {
+            const float v = __shfl_up(cj, o, kQ);
+            if (jj >= o) cj += v;
+        }
+        const float last = __shfl(cj, kQ - 1, kQ);
+        const float wj = ex2(last - cj) * dv;
+        if (tid < kQ) {
+            lds[C_::oCum + tid] = cj;
+            lds[C_::oDv + tid] = dv;
+        }
         float* xt = lds + C_::oXt;
 #pragma unroll
         for (int k = 0; k < kXv; k++) {
@@ -154,24 +172,11 @@ struct Ssd {
             const int j = i % kQ, n4 = (i / kQ) * 4;
             *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = st.bv[k];
             *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = st.cv[k];
-            bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x;
-            bt[(n4 + 1) * C_::LDQ + j] = st.bv[k].y;
-            bt[(n4 + 2) * C_::LDQ + j] = st.bv[k].z;
-            bt[(n4 + 3) * C_::LDQ + j] = st.bv[k].w;
-        }
-        if (tid < kQ) {
-            const int64_t t = t0 + tid;
-            const float dv = t < a.L ? softplus(st.dt + bias) : 0.0f;
-            float c = dv * A2;
-#pragma unroll
-            for (int o = 1; o < kQ; o <<= 1) {
-                const float v = __shfl_up(c, o, kQ);
-                if (tid >= o) c += v;
-            }
-            const float last = __shfl(c, kQ - 1, kQ);
-            lds[C_::oCum + tid] = c;
-            lds[C_::oDv + tid] = dv;
-            lds[C_::oW + tid] = ex2(last - c) * dv;
+            // Bt holds B^T already weighted by w_j (its only use)
+            bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x * wj;
+            bt[(n4 + 1) * C_::LDQ + j] = st.bv[k].y * wj;
+            bt[(n4 + 2) * C_::LDQ + j] = st.bv[k].z * wj;
+            bt[(n4 + 3) * C_::LDQ + j] = st.bv[k].w * wj;
         }
         __syncthreads();
     }
@@ -278,18 +283,15 @@ struct Ssd {
         const float decay = ex2(lds[C_::oCum + kQ - 1]);
         const float* Bt = lds + C_::oBt;
         const float* Xt = lds + C_::oXt;
-        const float* w = lds + C_::oW;
 #pragma unroll
         for (int c = 0; c < C_::CTW; c++) {
             const int ct = wave * C_::CTW + c;
             if (ct >= C_::CT) break;
             const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
-            float4 xb[kQ / 16], wv[kQ / 16];
+            float4 xb[kQ / 16];
 #pragma unroll
-            for (int kt = 0; kt < kQ / 16; kt++) {
+            for (int kt = 0; kt < kQ / 16; kt++)
                 xb[kt] = *reinterpret_cast<const float4*>(Xr + 16 * kt);
-                wv[kt] = *reinterpret_cast<const float4*>(w + 16 * kt + 4 * g4);
-            }
 #pragma unroll
             for (int tn = 0; tn < C_::NT; tn++) {
                 v4f s = S[c][tn] * decay;
@@ -297,10 +299,10 @@ struct Ssd {
 #pragma unroll
                 for (int kt = 0; kt < kQ / 16; kt++) {
                     const float4 ba = *reinterpret_cast<const float4*>(Br + 16 * kt);
-                    s = mfma(ba.x * wv[kt].x, xb[kt].x, s);
-                    s = mfma(ba.y * wv[kt].y, xb[kt].y, s);
-                    s = mfma(ba.z * wv[kt].z, xb[kt].z, s);
-                    s = mfma(ba.w * wv[kt].w, xb[kt].w, s);
+                    s = mfma(ba.x, xb[kt].x, s);
+                    s = mfma(ba.y, xb[kt].y, s);
+                    s = mfma(ba.z, xb[kt].z, s);
+                    s = mfma(ba.w, xb[kt].w, s);
                 }
                 S[c][tn] = s;
             }
