@@ -265,15 +265,18 @@ struct Ssd {
                 y1 = mfma(c1.w * f1, S[c][tn][3], y1);
             }
             const int p = 16 * ct + q16;
+            // x of rows 4 g4 .. 4 g4 + 3 (and 16 more) of column p: one
+            // 16-byte read each
+            const float4 x0 = *reinterpret_cast<const float4*>(Xt + p * C_::LDQ + 4 * g4);
+            const float4 x1 = *reinterpret_cast<const float4*>(Xt + p * C_::LDQ + 16 + 4 * g4);
+            const float xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int i0 = 4 * g4 + r, i1 = 16 + 4 * g4 + r;
                 if (i0 < nout)
-                    a.y[row(t0 + i0) * HP + h * P + p] =
-                        __builtin_fmaf(dskip, Xt[p * C_::LDQ + i0], y0[r]);
+                    a.y[row(t0 + i0) * HP + h * P + p] = __builtin_fmaf(dskip, xs0[r], y0[r]);
                 if (i1 < nout)
-                    a.y[row(t0 + i1) * HP + h * P + p] =
-                        __builtin_fmaf(dskip, Xt[p * C_::LDQ + i1], y1[r]);
+                    a.y[row(t0 + i1) * HP + h * P + p] = __builtin_fmaf(dskip, xs1[r], y1[r]);
             }
         }
     }
