@@ -198,13 +198,14 @@ def ssd_extras(stream, reps=5):
     t = _time_ms(lambda: mss.ssd_scan(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D_vec"],
                                       d["dt_bias"], None, batch=w.batch, seq_len=w.seq_len,
                                       head_dim=w.head_dim, d_state=w.d_state,
-                                      n_groups=w.n_groups, out=y, stream=stream),
+                                      n_groups=w.n_groups, disc="euler", out=y,
+                                      stream=stream),
                  stream, reps)
     fl = ssd_flops(w)
     bytes_ = 4 * (2 * w.M * w.n_heads * w.head_dim + w.M * w.n_heads
                   + 2 * w.M * w.n_groups * w.d_state)
     tf = fl / t / 1e9
-    return {"workload": w.name, "ms": t, "algorithmic_flops": fl, "TFLOPs": tf,
+    return {"workload": w.name, "disc": "euler", "ms": t, "algorithmic_flops": fl, "TFLOPs": tf,
             "frac_of_fp32_mfma_peak": tf / MFMA_F32_PEAK_TFLOPS,
             "algorithmic_bytes": bytes_, "GBps": bytes_ / t / 1e6,
             "tokens_per_s": w.M / (t / 1e3)}

@@ -223,8 +223,10 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
  * show its arithmetic; this is the plainest reading consistent with the
  * Mamba-1 path: per batch row and head h of group g = h / (H/G),
  *   dv = softplus(dt[r, h] + dt_bias[h]),  A_h = -exp(clamp(A_log[h], -10, 5))
- *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + dv x[r, h*P + p] B[r, g*N + n]
+ *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + f x[r, h*P + p] B[r, g*N + n]
  *   y[r, h*P + p] = sum_n C[r, g*N + n] S_h[p, n] + D_vec[h] x[r, h*P + p]
+ * with f = dv (MSS_DISC_EULER, the Mamba-2 form) or expm1(dv A_h) / A_h
+ * (MSS_DISC_ZOH, the discretisation of the pages' Mamba-1 path).
  * Computed in chunks on the matrix cores (fp32 MFMA); segments processed in
  * parallel drop contributions that have decayed by more than 2^-30. */
 typedef struct mss_ssd_dims {
@@ -242,7 +244,7 @@ typedef struct mss_ssd_dims {
  *   D_vec, dt_bias (H), may be NULL (= 0);
  *   h0, h_last (B, H, P, N), may be NULL (h0 = 0 / not written).
  * A sequence of length 0 still defines h_last (= h0, or zeros).          */
-int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, const float* A_log,
+int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float* dt, const float* A_log,
                  const float* B, const float* C, const float* D_vec, const float* dt_bias,
                  const float* h0, float* y, float* h_last, hipStream_t stream);
 

@@ -103,7 +103,7 @@ def lib():
         L.mss_workspace_bytes.argtypes = [dp, i, ctypes.POINTER(sz)]
         L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
         L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
-        L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims)] + [p] * 11
+        L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims), i] + [p] * 11
         for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
                   "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
                   "mss_workspace_bytes", "mss_selective_scan_backward",
@@ -375,7 +375,7 @@ def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, workspace=Non
 
 
 def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, seq_len,
-             head_dim, d_state, n_groups=1, h_last=False, out=None, stream=None):
+             head_dim, d_state, n_groups=1, disc, h_last=False, out=None, stream=None):
     """Mamba-2 SSD scan: y (batch*seq_len, H*head_dim) and, when ``h_last`` is
     True (or a tensor), the final state (batch, H, head_dim, d_state)."""
     H = A_log.shape[0]
@@ -386,7 +386,7 @@ def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, se
           (_empty((batch, H, P, N), x) if h_last else None))
     dims = make_ssd_dims(batch, seq_len, H, P, N, G)
     _check("mss_ssd_scan", lib().mss_ssd_scan(
-        ctypes.byref(dims), _ptr(x, "x", (M, H * P)), _ptr(dt, "dt", (M, H)),
+        ctypes.byref(dims), _disc(disc), _ptr(x, "x", (M, H * P)), _ptr(dt, "dt", (M, H)),
         _ptr(A_log, "A_log", (H,)), _ptr(B, "B", (M, G * N)), _ptr(C, "C", (M, G * N)),
         _ptr(D_vec, "D_vec", (H,), False), _ptr(dt_bias, "dt_bias", (H,), False),
         _ptr(h0, "h0", (batch, H, P, N), False), _ptr(y, "y", (M, H * P)),

@@ -5,10 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mss.h"
+
 namespace mss {
 
 // One workgroup per (batch row, head, segment of seg_chunks chunks).
 struct SsdArgs {
+    int disc;              // MSS_DISC_ZOH or MSS_DISC_EULER
     int64_t B, L, H, P, N, G;
     int64_t nseg, seg_chunks;
     const float* x;        // (M, H*P)

@@ -546,7 +546,7 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
-int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, const float* A_log,
+int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float* dt, const float* A_log,
                  const float* B, const float* C, const float* D_vec, const float* dt_bias,
                  const float* h0, float* y, float* h_last, hipStream_t stream) {
     if (!dims || dims->struct_size != static_cast<int32_t>(sizeof(mss_ssd_dims)) ||
@@ -556,6 +556,7 @@ int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, cons
     const int64_t N = dims->d_state, G = dims->n_groups;
     if (Bt < 0 || L < 0 || H < 1 || G < 1 || H % G != 0 || !mss::ssd_supported(P, N))
         return MSS_EINVAL;
+    if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
     int64_t M, MHP, MH, MGN, BHPN;
     if (!count(M, {Bt, L}) || !count(MHP, {Bt, L, H, P}) || !count(MH, {Bt, L, H}) ||
         !count(MGN, {Bt, L, G, N}) || !count(BHPN, {Bt, H, P, N}))
@@ -595,7 +596,7 @@ int mss_ssd_scan(const mss_ssd_dims* dims, const float* x, const float* dt, cons
     const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
     nseg = (nchunks + seg_chunks - 1) / seg_chunks;
     if (bh * nseg > INT32_MAX) return MSS_EINVAL;
-    const mss::SsdArgs a{Bt, L, H, P, N, G, nseg, seg_chunks, x, dt, A_log, B, C,
+    const mss::SsdArgs a{disc, Bt, L, H, P, N, G, nseg, seg_chunks, x, dt, A_log, B, C,
                          D_vec, dt_bias, h0, y, h_last};
     const hipError_t e = mss::launch_ssd(a, stream);
     return e == hipSuccess ? MSS_OK : hip_fail(e);

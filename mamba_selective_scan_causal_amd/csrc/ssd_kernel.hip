@@ -6,13 +6,15 @@
 // x (M, H*P), dt (M, H), B and C (M, G*N) split from the projections): per
 // batch row and head h (group g = h / (H/G)), with A_h = -exp(clamp(A_log_h))
 // and dv_t = softplus(dt_t + dt_bias_h),
-//   S_t = exp(dv_t A_h) S_{t-1} + dv_t x_t B_t^T      (S is P x N)
+//   S_t = exp(dv_t A_h) S_{t-1} + f_t x_t B_t^T      (S is P x N)
 //   y_t = S_t C_t + D_h x_t
+// where f_t = dv_t (EULER) or expm1(dv_t A_h) / A_h (ZOH), the two
+// discretisations of the Mamba-1 path.
 //
 // Chunked form.  Over a chunk of Q steps with c_i = sum_{r<=i} dv_r A_h:
 //   Y    = (L o C B^T) X  +  diag(e^{c}) C S_in^T...  (per head, P columns)
-//   with L_ij = e^{c_i - c_j} dv_j for i >= j (else 0), and
-//   S_out = e^{c_{Q-1}} S_in + sum_j e^{c_{Q-1} - c_j} dv_j x_j B_j^T.
+//   with L_ij = e^{c_i - c_j} f_j for i >= j (else 0), and
+//   S_out = e^{c_{Q-1}} S_in + sum_j e^{c_{Q-1} - c_j} f_j x_j B_j^T.
 // Every product is a dense contraction: v_mfma_f32_16x16x4f32 (fp32 in, fp32
 // accumulate).  Indexing the summation as k = 4 (lane / 16) + step makes the
 // accumulator layout of an S tile (rows n, columns p: lane l holds
@@ -71,12 +73,14 @@ struct Ssd {
     const int64_t b, h, g;
     float* lds;
     const float A2;        // A_h log2(e)
+    const float Ainv;      // 1 / A_h
     const float bias, dskip;
     const uint32_t lane, wave, q16, g4;   // lane, wave, lane % 16, lane / 16
 
     __device__ Ssd(const SsdArgs& a_, int64_t b_, int64_t h_, float* lds_)
         : a(a_), b(b_), h(h_), g(h_ / (a_.H / a_.G)), lds(lds_),
-          A2(a_cont(a_.A_log[h_]) * kLog2e), bias(a_.dt_bias ? a_.dt_bias[h_] : 0.0f),
+          A2(a_cont(a_.A_log[h_]) * kLog2e), Ainv(1.0f / a_cont(a_.A_log[h_])),
+          bias(a_.dt_bias ? a_.dt_bias[h_] : 0.0f),
           dskip(a_.D_vec ? a_.D_vec[h_] : 0.0f), lane(threadIdx.x & 63u),
           wave(threadIdx.x >> 6), q16(threadIdx.x & 15u), g4((threadIdx.x & 63u) >> 4) {}
 
@@ -136,22 +140,30 @@ struct Ssd {
     // prefix c (log2 units) and the state weights.  Ends with a barrier.
     __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
         const int tid = threadIdx.x;
-        // dv, the decay prefix c (log2 units) and the state weight
-        // w_j = 2^{c_{Q-1} - c_j} dv_j of this thread's step j = tid % kQ,
-        // computed by every 32-lane half (shuffles of width kQ).
+        // dv, the input factor f, the decay prefix c (log2 units) and the
+        // state weight w_j = 2^{c_{Q-1} - c_j} f_j of this thread's step
+        // j = tid % kQ, computed by every 32-lane half (shuffles of width kQ).
         const int jj = tid % kQ;
         const float dv = t0 + jj < a.L ? softplus(st.dt + bias) : 0.0f;
         float cj = dv * A2;
+        float fj = dv;
+        if (a.disc == MSS_DISC_ZOH) {
+            // expm1(dv A) / A; the cubic below |dv A| = 2^-6 keeps it exact
+            // to ~2e-7 relative where aBar - 1 would cancel
+            const float xn = cj * kLn2;
+            const float p3 = xn * __builtin_fmaf(xn, __builtin_fmaf(xn, 1.0f / 6.0f, 0.5f), 1.0f);
+            fj = (__builtin_fabsf(xn) < 0.015625f ? p3 : ex2(cj) - 1.0f) * Ainv;
+        }
 #pragma unroll
         for (int o = 1; o < kQ; o <<= 1) {
             const float v = __shfl_up(cj, o, kQ);
             if (jj >= o) cj += v;
         }
         const float last = __shfl(cj, kQ - 1, kQ);
-        const float wj = ex2(last - cj) * dv;
+        const float wj = ex2(last - cj) * fj;
         if (tid < kQ) {
             lds[C_::oCum + tid] = cj;
-            lds[C_::oDv + tid] = dv;
+            lds[C_::oDv + tid] = fj;
         }
         float* xt = lds + C_::oXt;
 #pragma unroll

@@ -62,7 +62,7 @@ def _declare(lib):
                                           p, p, p, i64, p, p, p, i32]
     lib.oracle_selective_scan_backward.argtypes = [i64, i64, i64, i64, i32] + [p] * 17 + [i32]
     lib.oracle_conv1d_silu_backward.argtypes = [i64, i64, i64, i64] + [p] * 7 + [i32]
-    lib.oracle_ssd_scan.argtypes = [i64] * 6 + [p] * 10 + [i32]
+    lib.oracle_ssd_scan.argtypes = [i64] * 6 + [i32] + [p] * 10 + [i32]
     for f in (lib.oracle_conv1d_silu, lib.oracle_selective_scan, lib.oracle_mamba1_core,
               lib.oracle_selective_step, lib.oracle_selective_scan_backward,
               lib.oracle_conv1d_silu_backward, lib.oracle_ssd_scan):
@@ -248,7 +248,7 @@ def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, nthreads=0, l
 
 
 def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, seq_len,
-             n_heads, head_dim, d_state, n_groups=1, h_last=False, nthreads=0, lib=None):
+             n_heads, head_dim, d_state, n_groups=1, disc, h_last=False, nthreads=0, lib=None):
     """Mamba-2 SSD scan in fp64.  Returns (y (M, H*P), h_last (batch, H, P, N) or None)."""
     H, P, N, G = n_heads, head_dim, d_state, n_groups
     M = batch * seq_len
@@ -257,7 +257,7 @@ def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, se
             _f32(dt_bias, "dt_bias", (H,)), _f32(h0, "h0", (batch, H, P, N))]
     y = np.empty((M, H * P))
     hl = np.empty((batch, H, P, N)) if h_last else None
-    rc = (lib or load()).oracle_ssd_scan(batch, seq_len, H, P, N, G, *map(_ptr, args), _ptr(y),
+    rc = (lib or load()).oracle_ssd_scan(batch, seq_len, H, P, N, G, _disc(disc), *map(_ptr, args), _ptr(y),
                                          _ptr(hl), nthreads)
     if rc != 0:
         raise ValueError(f"oracle_ssd_scan failed ({rc})")

@@ -535,15 +535,18 @@ int oracle_conv1d_silu_backward(int64_t B, int64_t L, int64_t D, int64_t K,
  *   H heads of P channels (x column h*P + p), G groups of N states sharing
  *   B and C (head h uses group h / (H / G), column g*N + n);
  *   dv = softplus(dt[r, h] + dt_bias[h]),  A_h = -exp(clamp(A_log[h], -10, 5))
- *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + dv x[r, h*P + p] B[r, g*N + n]
+ *   S_h[p, n] <- exp(dv A_h) S_h[p, n] + f x[r, h*P + p] B[r, g*N + n]
+ *   with the input factor f = dv (EULER) or expm1(dv A_h) / A_h (ZOH), the
+ *   two discretisations of the Mamba-1 path
  *   y[r, h*P + p] = sum_n C[r, g*N + n] S_h[p, n] + D[h] x[r, h*P + p]
  * State (B, H, P, N), starting at h0 or 0.  One (b, h) at a time, time in
  * order, fp64.                                                              */
-int oracle_ssd_scan(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+int oracle_ssd_scan(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int disc,
                     const float* x, const float* dt, const float* A_log, const float* Bm,
                     const float* Cm, const float* Dv, const float* dt_bias, const float* h0,
                     double* y, double* h_last, int nthreads) {
     if (B < 0 || L < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return -1;
+    if (disc != ORACLE_DISC_ZOH && disc != ORACLE_DISC_EULER) return -1;
     if (!x || !dt || !A_log || !Bm || !Cm || !y) return -1;
     const int64_t HP = H * P, GN = G * N, hpg = H / G;
     int nt = set_threads(nthreads);
@@ -568,12 +571,13 @@ int oracle_ssd_scan(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64
                 const int64_t r = b * L + t;
                 const double dv = softplus((double)dt[r * H + h] + bias);
                 const double a = exp(dv * A);
+                const double f = b_bar(disc, dv, A, 1.0);
                 for (int64_t p = 0; p < P; p++) {
                     const double xv = (double)x[r * HP + h * P + p];
                     double acc = Dh * xv;
                     for (int64_t n = 0; n < N; n++) {
                         double* s = &S[p * N + n];
-                        *s = a * *s + dv * xv * (double)Bm[r * GN + g * N + n];
+                        *s = a * *s + f * xv * (double)Bm[r * GN + g * N + n];
                         acc += (double)Cm[r * GN + g * N + n] * *s;
                     }
                     y[r * HP + h * P + p] = acc;

@@ -663,20 +663,25 @@ def _ssd_inputs(seed, B, L, H, P, N, G, *, h0=True, bias=True):
     )
 
 
-def _ssd(orc, inp, B, L, H, P, N, G, **kw):
+def _ssd(orc, inp, B, L, H, P, N, G, disc=EULER, **kw):
     return orc.ssd_scan(inp["x"], inp["dt"], inp["A_log"], inp["B"], inp["C"], inp["D_vec"],
                         inp["dt_bias"], inp["h0"], batch=B, seq_len=L, n_heads=H, head_dim=P,
-                        d_state=N, n_groups=G, h_last=True, **kw)
+                        d_state=N, n_groups=G, disc=disc, h_last=True, **kw)
 
 
-def pin_ssd_is_mamba1_euler_per_channel(orc):
-    # Channel (h, p) of the SSD scan is the Mamba-1 EULER scan of one channel
-    # whose N states all have A_h, on delta = dt + dt_bias, with the B and C
-    # of the head's group: run the (separately pinned) Mamba-1 oracle group by
-    # group and compare y and the final state.
+def pin_ssd_is_mamba1_per_channel(orc):
+    # Channel (h, p) of the SSD scan is the Mamba-1 scan (same discretisation)
+    # of one channel whose N states all have A_h, on delta = dt + dt_bias,
+    # with the B and C of the head's group: run the (separately pinned)
+    # Mamba-1 oracle group by group and compare y and the final state.
+    for disc in (EULER, ZOH):
+        _ssd_vs_mamba1(orc, disc)
+
+
+def _ssd_vs_mamba1(orc, disc):
     B, L, H, P, N, G = 2, 23, 6, 3, 5, 3
     inp = _ssd_inputs(61, B, L, H, P, N, G)
-    y, hl = _ssd(orc, inp, B, L, H, P, N, G)
+    y, hl = _ssd(orc, inp, B, L, H, P, N, G, disc=disc)
     hpg = H // G
     for g in range(G):
         heads = range(g * hpg, (g + 1) * hpg)
@@ -691,7 +696,7 @@ def pin_ssd_is_mamba1_euler_per_channel(orc):
             inp["x"][:, cols], _f32(delta), _f32(alog), inp["B"][:, g * N:(g + 1) * N],
             inp["C"][:, g * N:(g + 1) * N], np.repeat(inp["D_vec"][list(heads)], P), None,
             inp["h0"][:, list(heads)].reshape(B, hpg * P, N), batch=B, seq_len=L,
-            disc=EULER, h_last=True)
+            disc=disc, h_last=True)
         _close(y[:, cols], y1, 1e-6, 1e-6, f"ssd vs mamba1, group {g}")
         _close(hl[:, list(heads)].reshape(B, hpg * P, N), hl1, 1e-6, 1e-6,
                f"ssd h_last vs mamba1, group {g}")
@@ -704,17 +709,19 @@ def pin_ssd_exact_shift_of_dt(orc):
     inp = _ssd_inputs(62, B, L, H, P, N, G)
     inp["dt"] = _f32(np.round(inp["dt"] * 64) / 64)
     inp["dt_bias"] = _f32(np.round(inp["dt_bias"] * 64) / 64)
-    y, hl = _ssd(orc, inp, B, L, H, P, N, G)
-    moved = dict(inp, dt=_f32(inp["dt"] + inp["dt_bias"][None, :]), dt_bias=None)
-    y2, hl2 = _ssd(orc, moved, B, L, H, P, N, G)
-    assert np.array_equal(y, y2) and np.array_equal(hl, hl2)
+    for disc in (EULER, ZOH):
+        y, hl = _ssd(orc, inp, B, L, H, P, N, G, disc=disc)
+        moved = dict(inp, dt=_f32(inp["dt"] + inp["dt_bias"][None, :]), dt_bias=None)
+        y2, hl2 = _ssd(orc, moved, B, L, H, P, N, G, disc=disc)
+        assert np.array_equal(y, y2) and np.array_equal(hl, hl2)
 
 
 def pin_ssd_quadratic_form(orc):
     # The scan equals its unrolled (attention-like) form, evaluated here
     # directly in fp64 for every output:
-    #   y[t,h,p] = sum_{s<=t} (C_t . B_s) exp(A_h sum_{r=s+1..t} dv_r) dv_s x[s,h,p]
+    #   y[t,h,p] = sum_{s<=t} (C_t . B_s) exp(A_h sum_{r=s+1..t} dv_r) f_s x[s,h,p]
     #              + sum_n C_t,n exp(A_h sum_{r<=t} dv_r) h0[h,p,n] + D_h x[t,h,p]
+    # with f = dv (EULER), checked here; ZOH's f is pinned by the Mamba-1 pin.
     B, L, H, P, N, G = 2, 12, 4, 3, 4, 2
     inp = _ssd_inputs(63, B, L, H, P, N, G)
     y, hl = _ssd(orc, inp, B, L, H, P, N, G)

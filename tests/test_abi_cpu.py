@@ -278,7 +278,9 @@ def ssd_call(L, dims, **over):
     args = dict(x=fake(1), dt=fake(2), A_log=fake(3), B=fake(4), C=fake(5), D=fake(6),
                 bias=fake(7), h0=None, y=fake(8), h_last=None)
     args.update(over)
-    return L.mss_ssd_scan(ctypes.byref(dims) if dims is not None else None, *args.values(), None)
+    disc = args.pop("disc", 1)
+    return L.mss_ssd_scan(ctypes.byref(dims) if dims is not None else None, disc,
+                          *args.values(), None)
 
 
 def test_ssd_validation(L):
@@ -291,6 +293,7 @@ def test_ssd_validation(L):
     assert ssd_call(L, mss.make_ssd_dims(2, 64, 8, 64, 96)) == EINVAL      # d_state
     assert ssd_call(L, mss.make_ssd_dims(2, 64, 8, 64, 128, 3)) == EINVAL  # G does not divide H
     assert ssd_call(L, mss.make_ssd_dims(2, 64, 0, 64, 128)) == EINVAL
+    assert ssd_call(L, d, disc=2) == EINVAL
     for name in ("x", "dt", "A_log", "B", "C", "y"):
         assert ssd_call(L, d, **{name: None}) == EINVAL, name
     assert ssd_call(L, d, y=fake(1)) == EALIAS

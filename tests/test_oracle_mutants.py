@@ -78,16 +78,18 @@ MUTANTS = [
     ("ssd_group_of_head", "g = h / hpg;", "g = h % G;"),
     ("ssd_dt_bias_dropped", "const double bias = dt_bias ? (double)dt_bias[h] : 0.0;",
      "const double bias = 0.0;"),
-    ("ssd_input_without_dv", "*s = a * *s + dv * xv * (double)Bm[r * GN + g * N + n];",
+    ("ssd_input_without_factor", "*s = a * *s + f * xv * (double)Bm[r * GN + g * N + n];",
      "*s = a * *s + xv * (double)Bm[r * GN + g * N + n];"),
+    ("ssd_factor_ignores_disc", "const double f = b_bar(disc, dv, A, 1.0);",
+     "const double f = dv;"),
     ("ssd_decay_without_dv", "const double a = exp(dv * A);", "const double a = exp(A);"),
     ("ssd_output_uses_B", "acc += (double)Cm[r * GN + g * N + n] * *s;",
      "acc += (double)Bm[r * GN + g * N + n] * *s;"),
     ("ssd_skip_dropped", "double acc = Dh * xv;", "double acc = 0.0;"),
     ("ssd_h0_ignored", "S[i] = h0 ? (double)h0[bh * P * N + i] : 0.0;", "S[i] = 0.0;"),
     ("ssd_output_before_update",
-     "*s = a * *s + dv * xv * (double)Bm[r * GN + g * N + n];\n                        acc += (double)Cm[r * GN + g * N + n] * *s;",
-     "acc += (double)Cm[r * GN + g * N + n] * *s;\n                        *s = a * *s + dv * xv * (double)Bm[r * GN + g * N + n];"),
+     "*s = a * *s + f * xv * (double)Bm[r * GN + g * N + n];\n                        acc += (double)Cm[r * GN + g * N + n] * *s;",
+     "acc += (double)Cm[r * GN + g * N + n] * *s;\n                        *s = a * *s + f * xv * (double)Bm[r * GN + g * N + n];"),
 ]
 
 

@@ -20,7 +20,7 @@ def _announce(request):
     yield
 
 
-def run_ssd(inp, w, *, dvec=True, bias=True, h0=True):
+def run_ssd(inp, w, *, disc="euler", dvec=True, bias=True, h0=True):
     import torch
     d = {k: dev(v) for k, v in inp.items()}
     y = nan_like((w.M, w.n_heads * w.head_dim))
@@ -28,17 +28,17 @@ def run_ssd(inp, w, *, dvec=True, bias=True, h0=True):
     mss.ssd_scan(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D_vec"] if dvec else None,
                  d["dt_bias"] if bias else None, d["h0"] if (h0 and "h0" in d) else None,
                  batch=w.batch, seq_len=w.seq_len, head_dim=w.head_dim, d_state=w.d_state,
-                 n_groups=w.n_groups, h_last=hl, out=y)
+                 n_groups=w.n_groups, disc=disc, h_last=hl, out=y)
     torch.cuda.synchronize()
     return host(y), host(hl)
 
 
-def oracle_ssd(inp, w, *, dvec=True, bias=True, h0=True):
+def oracle_ssd(inp, w, *, disc="euler", dvec=True, bias=True, h0=True):
     return oracle.ssd_scan(inp["x"], inp["dt"], inp["A_log"], inp["B"], inp["C"],
                            inp["D_vec"] if dvec else None, inp["dt_bias"] if bias else None,
                            inp.get("h0") if h0 else None, batch=w.batch, seq_len=w.seq_len,
                            n_heads=w.n_heads, head_dim=w.head_dim, d_state=w.d_state,
-                           n_groups=w.n_groups, h_last=True)
+                           n_groups=w.n_groups, disc=disc, h_last=True)
 
 
 def check(w, inp=None, **kw):
@@ -50,9 +50,10 @@ def check(w, inp=None, **kw):
     announce(f"errors y={e1:.1e} h_last={e2:.1e}")
 
 
+@pytest.mark.parametrize("disc", ("euler", "zoh"))
 @pytest.mark.parametrize("w", [gen.SSD_TINY, gen.SSD_SMALL], ids=lambda w: w.name)
-def test_ssd_workloads(w):
-    check(w)
+def test_ssd_workloads(w, disc):
+    check(w, disc=disc)
 
 
 SSD_EDGE = [
@@ -73,6 +74,8 @@ SSD_EDGE = [
 @pytest.mark.parametrize("name,over", SSD_EDGE, ids=[e[0] for e in SSD_EDGE])
 def test_ssd_edge_cases(name, over):
     check(gen.SSD_SMALL.with_(**over))
+    if name in ("ragged_len", "many_segments", "tiny_steps"):
+        check(gen.SSD_SMALL.with_(**over), disc="zoh")
 
 
 def test_ssd_no_skip_no_bias_no_h0_and_dt_bias():
@@ -90,6 +93,7 @@ def test_ssd_slow_decay_full_replay():
     inp = gen.generate_ssd(w)
     inp["A_log"] = np.array([-12.0, 0.5], dtype=np.float32)
     check(w, inp=inp)
+    check(w, inp=inp, disc="zoh")
 
 
 def test_ssd_empty_and_deterministic():
@@ -101,7 +105,7 @@ def test_ssd_empty_and_deterministic():
     dt = torch.empty((0, 2), device="cuda")
     bc = torch.empty((0, 128), device="cuda")
     y, hl = mss.ssd_scan(x, dt, d["A_log"], bc, bc, d["D_vec"], None, d["h0"], batch=2,
-                         seq_len=0, head_dim=64, d_state=128, h_last=True)
+                         seq_len=0, head_dim=64, d_state=128, disc="euler", h_last=True)
     torch.cuda.synchronize()
     assert np.array_equal(host(hl), inp["h0"].astype(np.float64))
     w = gen.SSD_SMALL.with_(batch=1, seq_len=1000, n_heads=3)
@@ -126,5 +130,10 @@ def test_ssd_full_size_sampled_heads():
                dt_bias=inp["dt_bias"][heads])
     ws = w.with_(n_heads=len(heads))
     oy, ohl = oracle_ssd(sub, ws, h0=False)
+    # the same launch configuration in the other discretisation
+    y2, hl2 = run_ssd(inp, w, disc="zoh")
+    oy2, ohl2 = oracle_ssd(sub, ws, disc="zoh", h0=False)
+    assert_close(y2[:, cols], oy2, "y (zoh)")
+    assert_close(hl2[:, heads], ohl2, "h_last (zoh)")
     assert_close(y[:, cols], oy, "y")
     assert_close(hl[:, heads], ohl, "h_last")
