@@ -430,13 +430,21 @@ int oracle_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, i
     if (!du || !ddelta || !dA_log || !dB || !dC || !dD) return -1;
     if (z && !dz) return -1;
     bwd_args a = {B, L, D, N, disc, u, delta, A_log, Bm, Cm, Dv, z, h0, dout};
-    const int64_t cols = B * D;
-    double* colB = (double*)calloc((size_t)(cols * L * N + 1), sizeof(double));
-    double* colC = (double*)calloc((size_t)(cols * L * N + 1), sizeof(double));
-    double* colA = (double*)calloc((size_t)(cols * N + 1), sizeof(double));
-    double* colD = (double*)calloc((size_t)(cols + 1), sizeof(double));
-    if (!colB || !colC || !colA || !colD) {
-        free(colB); free(colC); free(colA); free(colD);
+    /* The sums over d of the per-column dB, dC rows are taken in a fixed
+     * order without storing every column: the channels of a batch row are
+     * cut into blocks of 64, each block adds its columns in
+     * channel order into a block buffer (L*N), and the blocks are added in
+     * order at the end.  Bitwise identical for any thread count. */
+    const int64_t BLK = 64;
+    const int64_t nblk_b = D > 0 ? (D + BLK - 1) / BLK : 0;
+    const int64_t nblk = B * nblk_b;
+    const int64_t LN = L * N;
+    double* blkB = (double*)calloc((size_t)(nblk * LN + 1), sizeof(double));
+    double* blkC = (double*)calloc((size_t)(nblk * LN + 1), sizeof(double));
+    double* colA = (double*)calloc((size_t)(B * D * N + 1), sizeof(double));
+    double* colD = (double*)calloc((size_t)(B * D + 1), sizeof(double));
+    if (!blkB || !blkC || !colA || !colD) {
+        free(blkB); free(blkC); free(colA); free(colD);
         return -2;
     }
     int nt = set_threads(nthreads);
@@ -445,30 +453,40 @@ int oracle_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, i
     {
         double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
         double* ys = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-        if (!hs || !ys) {
+        double* cb = (double*)malloc(sizeof(double) * (size_t)(LN > 0 ? LN : 1));
+        double* cc = (double*)malloc(sizeof(double) * (size_t)(LN > 0 ? LN : 1));
+        if (!hs || !ys || !cb || !cc) {
 #pragma omp atomic write
             err = -2;
         }
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t c = 0; c < cols; c++) {
-            if (!hs || !ys) continue;
-            const int64_t b = c / D, d = c % D;
-            scan_column_bwd(&a, b, d, hs, ys, du, ddelta, dz, dh0, colB + c * L * N,
-                            colC + c * L * N, colA + c * N, colD + c);
+        for (int64_t k = 0; k < nblk; k++) {
+            if (!hs || !ys || !cb || !cc) continue;
+            const int64_t b = k / nblk_b, d0 = (k % nblk_b) * BLK;
+            const int64_t d1 = d0 + BLK < D ? d0 + BLK : D;
+            for (int64_t d = d0; d < d1; d++) {
+                scan_column_bwd(&a, b, d, hs, ys, du, ddelta, dz, dh0, cb, cc,
+                                colA + (b * D + d) * N, colD + b * D + d);
+                for (int64_t i = 0; i < LN; i++) {
+                    blkB[k * LN + i] += cb[i];
+                    blkC[k * LN + i] += cc[i];
+                }
+            }
         }
         free(hs);
         free(ys);
+        free(cb);
+        free(cc);
     }
     if (err == 0) {
-        /* Cross-column sums in a fixed order: over d for dB, dC; over b for
-         * dA_log, dD. */
+        /* dB, dC: blocks of a batch row in order; dA_log, dD: over b. */
 #pragma omp parallel for schedule(static) num_threads(nt)
-        for (int64_t i = 0; i < B * L * N; i++) {
-            const int64_t b = i / (L * N), tn = i % (L * N);
+        for (int64_t i = 0; i < B * LN; i++) {
+            const int64_t b = i / LN, tn = i % LN;
             double sb = 0.0, sc = 0.0;
-            for (int64_t d = 0; d < D; d++) {
-                sb += colB[(b * D + d) * L * N + tn];
-                sc += colC[(b * D + d) * L * N + tn];
+            for (int64_t q = 0; q < nblk_b; q++) {
+                sb += blkB[(b * nblk_b + q) * LN + tn];
+                sc += blkC[(b * nblk_b + q) * LN + tn];
             }
             dB[i] = sb;
             dC[i] = sc;
@@ -485,7 +503,7 @@ int oracle_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, i
             dD[d] = s;
         }
     }
-    free(colB); free(colC); free(colA); free(colD);
+    free(blkB); free(blkC); free(colA); free(colD);
     return err;
 }
 

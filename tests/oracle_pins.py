@@ -599,6 +599,20 @@ def pin_scan_backward_long_memory(orc):
                 f"{disc} long d/d{name}{idx}: {grad[idx]:.10e} vs {fd:.10e}")
 
 
+def pin_scan_backward_thread_count(orc):
+    # The cross-channel sums run in a fixed order: any thread count gives
+    # bitwise the same gradients (D = 150 spans three channel blocks).
+    B, L, D, N = 2, 40, 150, 4
+    inp = _scan_inputs(71, B, L, D, N)
+    dout = _f32(_rng(72).standard_normal((B * L, D)))
+    args = (inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D_vec"], inp["z"],
+            inp["h0"], dout)
+    g1 = orc.selective_scan_backward(*args, batch=B, seq_len=L, disc=ZOH, nthreads=1)
+    g5 = orc.selective_scan_backward(*args, batch=B, seq_len=L, disc=ZOH, nthreads=5)
+    for k in g1:
+        assert np.array_equal(g1[k], g5[k]), k
+
+
 def pin_zoh_a_grad_tiny_step_closed_form(orc):
     # L = 1, h0 = 0, one state, ungated, no skip: y = C u B expm1(dv A) / A,
     # so dy/dA_log = C u B (x e^x - expm1(x)) / A with x = dv A, A = -e^A_log.

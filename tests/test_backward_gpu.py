@@ -82,11 +82,21 @@ def check_all(got, want, *, dvec=True, gated=True, tol=1e-4):
 
 
 @pytest.mark.parametrize("disc", DISCS)
-@pytest.mark.parametrize("w", [gen.TINY_CLAMP, gen.SMALL], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [gen.TINY_CLAMP, gen.SMALL, gen.MAMBA_130M], ids=lambda w: w.name)
 def test_scan_backward_workloads(w, disc):
     w = w.with_(h0=True)
     inp = _scan_inputs(w)
     check_all(run_bwd(inp, w, disc), oracle_bwd(inp, w, disc))
+
+
+def test_scan_backward_full_size():
+    """B4 L8192 D5120 N16, ZOH, gated, in the launch configuration bench.py
+    times: every gradient against the oracle run on the whole problem."""
+    w = gen.MAMBA_2P8B
+    inp = _scan_inputs(w)
+    got = run_bwd(inp, w, "zoh", h0=False)
+    want = oracle_bwd(inp, w, "zoh", h0=False)
+    check_all(got, want)
 
 
 BWD_EDGE = [
