@@ -94,20 +94,23 @@ __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
     p[K * kWave] = sb;
 }
 
+// One thread per (channel, row): row k < K is dw[d, k], row K is db[d]; the
+// groups of the channel's tile are added in order.
 __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(ConvBwdArgs a) {
-    const int64_t d = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-    if (d >= a.D) return;
+    const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    const int64_t rows = a.K + 1;
+    if (i >= a.D * rows) return;
+    const int64_t d = i / rows;
+    const int k = static_cast<int>(i - d * rows);
+    if (k == a.K && !a.db) return;
     const int64_t tile = d / kWave, lane = d - tile * kWave;
-    for (int k = 0; k <= a.K; k++) {
-        if (k == a.K && !a.db) break;
-        float acc = 0.0f;
-        for (int64_t g = 0; g < a.groups; g++)
-            acc += a.part[((tile * a.groups + g) * kPartRows + k) * kWave + lane];
-        if (k < a.K)
-            a.dw[d * a.K + k] = acc;
-        else
-            a.db[d] = acc;
-    }
+    const float* p = a.part + (tile * a.groups * kPartRows + k) * kWave + lane;
+    float acc = 0.0f;
+    for (int64_t g = 0; g < a.groups; g++) acc += p[g * kPartRows * kWave];
+    if (k < a.K)
+        a.dw[d * a.K + k] = acc;
+    else
+        a.db[d] = acc;
 }
 
 }  // namespace
@@ -121,8 +124,9 @@ hipError_t launch_conv1d_silu_bwd(const ConvBwdArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(conv_bwd_kernel<0>, dim3(grid), dim3(kWave), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3(static_cast<unsigned>((a.D + 255) / 256)),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL(conv_bwd_reduce_kernel,
+                       dim3(static_cast<unsigned>((a.D * (a.K + 1) + 255) / 256)), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
 }
 

@@ -395,6 +395,7 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
     if (MD > 0) {
         s = bwd_shape(dims);
         if (!bwd_layout(s, lay)) return MSS_EINVAL;
+        if (s.B * s.tiles_per_b * s.nseg > INT32_MAX) return MSS_EINVAL;   // grid size
         need = lay.total;
     }
     // The workspace is an output like the others: it may not overlap anything.
@@ -441,6 +442,7 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
     ck.out(dw_conv, D * K, true);
     ck.out(db_conv, D, false);
     const int64_t need = MD > 0 ? conv_bwd_bytes(dims) : 0;
+    if (MD > 0 && ((D + 63) / 64) * conv_bwd_groups(dims) > INT32_MAX) return MSS_EINVAL;
     if (need > 0 && workspace) ck.outs.push_back({workspace, need});
     st = ck.finish();
     if (st != MSS_OK) return st;
