@@ -87,7 +87,7 @@ def _time_ms(fn, stream, reps, warm=2):
     return a.elapsed_time(b) / reps
 
 
-def extras(w, d, y, disc, stream):
+def extras(w, d, y, disc, stream, with_oracle=True):
     """Side measurements: the other discretisation, the unfused path (conv
     kernel, then the scan on u), and the decode workload (256 sequences x
     5120 channels, 64 consecutive single-token steps)."""
@@ -124,8 +124,8 @@ def extras(w, d, y, disc, stream):
                                stream=stream)
 
     t64 = _time_ms(decode64, stream, 3, warm=1)
-    res["backward"] = backward_extras(w, d, stream)
-    res["ssd"] = ssd_extras(stream)
+    res["backward"] = backward_extras(w, d, stream, with_oracle=with_oracle)
+    res["ssd"] = ssd_extras(stream, with_oracle=with_oracle)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
     step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
@@ -135,7 +135,7 @@ def extras(w, d, y, disc, stream):
     return res
 
 
-def backward_extras(w, d, stream, reps=5):
+def backward_extras(w, d, stream, reps=5, with_oracle=True):
     """The backward passes on the same workload (ZOH): the scan backward
     (main kernel + fixed-order reduction kernel) on u = SiLU(conv(x)) with a
     seeded N(0, 1) output gradient, then the conv1d + SiLU backward."""
@@ -167,11 +167,37 @@ def backward_extras(w, d, stream, reps=5):
     # B, C in and dB, dC out per (m, n); x, du in and dx out for the conv
     sb_bytes = 4 * (7 * M * D + 4 * M * N + 3 * D * N + 2 * D)
     cb_bytes = 4 * (3 * M * D + 2 * D * (w.d_conv + 1))
-    return {"disc": "zoh", "workspace_bytes": nb,
-            "scan_backward_ms": t_sb, "scan_backward_algorithmic_bytes": sb_bytes,
-            "scan_backward_GBps": sb_bytes / t_sb / 1e6,
-            "conv1d_silu_backward_ms": t_cb, "conv1d_silu_backward_GBps": cb_bytes / t_cb / 1e6,
-            "total_ms": t_sb + t_cb}
+    res = {"disc": "zoh", "workspace_bytes": nb,
+           "scan_backward_ms": t_sb, "scan_backward_algorithmic_bytes": sb_bytes,
+           "scan_backward_GBps": sb_bytes / t_sb / 1e6,
+           "scan_backward_elements_per_s": M * D / (t_sb / 1e3),
+           "conv1d_silu_backward_ms": t_cb, "conv1d_silu_backward_GBps": cb_bytes / t_cb / 1e6,
+           "total_ms": t_sb + t_cb}
+    if with_oracle:
+        res["cpu_oracle"] = backward_oracle_rate(w)
+    return res
+
+
+def backward_oracle_rate(w, channels=512):
+    """The backward oracle as it stands on a bounded part of the same
+    workload: one batch row, the first `channels` channels, all L steps."""
+    import oracle
+    from mamba_selective_scan_causal_amd import inputs as gen
+    cores = len(os.sched_getaffinity(0))
+    sub = w.with_(batch=1, d_inner=channels)
+    inp = gen.generate(sub)
+    u = oracle.conv1d_silu(inp["x"], inp["w_conv"], inp["b_conv"], batch=1,
+                           seq_len=w.seq_len).astype(np.float32)
+    dout = gen.cotangent(sub)
+    t0 = time.perf_counter()
+    oracle.selective_scan_backward(u, inp["delta"], inp["A_log"], inp["B"], inp["C"],
+                                   inp["D_vec"], inp["z"], None, dout, batch=1,
+                                   seq_len=w.seq_len, disc="zoh", nthreads=cores)
+    t = time.perf_counter() - t0
+    el = w.seq_len * channels
+    return {"value": el / t, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 x {w.seq_len} x {channels} (b, t, d) of the same shape, fp64 C, "
+                      f"{t:.1f} s"}
 
 
 MFMA_F32_PEAK_TFLOPS = 157.3          # MI355X dense fp32 matrix, AMD published
@@ -186,7 +212,7 @@ def ssd_flops(w) -> int:
     return 2 * w.M * w.n_heads * (Q * N // 2 + Q * P // 2 + 2 * N * P)
 
 
-def ssd_extras(stream, reps=5):
+def ssd_extras(stream, reps=5, with_oracle=True):
     """The Mamba-2 SSD scan (mss_ssd_scan) on B4 L8192 H80 P64 N128 G1."""
     import torch
     import mamba_selective_scan_causal_amd as mss
@@ -205,10 +231,33 @@ def ssd_extras(stream, reps=5):
     bytes_ = 4 * (2 * w.M * w.n_heads * w.head_dim + w.M * w.n_heads
                   + 2 * w.M * w.n_groups * w.d_state)
     tf = fl / t / 1e9
-    return {"workload": w.name, "disc": "euler", "ms": t, "algorithmic_flops": fl, "TFLOPs": tf,
-            "frac_of_fp32_mfma_peak": tf / MFMA_F32_PEAK_TFLOPS,
-            "algorithmic_bytes": bytes_, "GBps": bytes_ / t / 1e6,
-            "tokens_per_s": w.M / (t / 1e3)}
+    res = {"workload": w.name, "disc": "euler", "ms": t, "algorithmic_flops": fl, "TFLOPs": tf,
+           "frac_of_fp32_mfma_peak": tf / MFMA_F32_PEAK_TFLOPS,
+           "algorithmic_bytes": bytes_, "GBps": bytes_ / t / 1e6,
+           "tokens_per_s": w.M / (t / 1e3),
+           "head_steps_per_s": w.M * w.n_heads / (t / 1e3)}
+    if with_oracle:
+        res["cpu_oracle"] = ssd_oracle_rate(w, inp)
+    return res
+
+
+def ssd_oracle_rate(w, inp, heads=4):
+    """The SSD oracle as it stands on `heads` heads of the same workload (all
+    batch rows and steps), on all host cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    hs = list(range(heads))
+    P = w.head_dim
+    cols = np.concatenate([np.arange(h * P, (h + 1) * P) for h in hs])
+    t0 = time.perf_counter()
+    oracle.ssd_scan(np.ascontiguousarray(inp["x"][:, cols]), np.ascontiguousarray(inp["dt"][:, hs]),
+                    inp["A_log"][hs], inp["B"], inp["C"], inp["D_vec"][hs], inp["dt_bias"][hs],
+                    None, batch=w.batch, seq_len=w.seq_len, n_heads=heads, head_dim=P,
+                    d_state=w.d_state, n_groups=w.n_groups, disc="euler", nthreads=cores)
+    t = time.perf_counter() - t0
+    return {"value": w.M * heads / t, "unit": "head_steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {w.n_heads} heads, all {w.batch} x {w.seq_len} steps, "
+                      f"fp64 C, {t:.1f} s"}
 
 
 def cpu_baseline(w, inp, disc, target_s=15.0):
@@ -270,10 +319,12 @@ def main():
     inp = gen.generate(w)
     d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
     if args.part == "ssd":
-        print(json.dumps(ssd_extras(torch.cuda.current_stream(), reps=max(args.steps, 1))))
+        print(json.dumps(ssd_extras(torch.cuda.current_stream(), reps=max(args.steps, 1),
+                                    with_oracle=not args.no_cpu_baseline)))
         return
     if args.part == "backward":
-        res = backward_extras(w, d, torch.cuda.current_stream(), reps=max(args.steps, 1))
+        res = backward_extras(w, d, torch.cuda.current_stream(), reps=max(args.steps, 1),
+                              with_oracle=not args.no_cpu_baseline)
         res["workload"] = w.name
         print(json.dumps(res))
         return
@@ -328,7 +379,7 @@ def main():
                      "kernel_digest": digest},
     }
     if not args.no_extras:
-        out["extra"] = extras(w, d, y, args.disc, stream)
+        out["extra"] = extras(w, d, y, args.disc, stream, with_oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.disc)
     print(json.dumps(out), flush=True)
