@@ -303,7 +303,7 @@ def main():
                          "the Mamba-2 SSD scan (one JSON line of timings, for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
