@@ -145,6 +145,7 @@ struct Bwd {
     const uint32_t half;
     const bool gated;
     float4* lds;               // 8 steps: B rows [0, 32), C rows [32, 64) (16 floats per row)
+    float4* acache;            // aBar of a block's 8 steps: [step][lane][2] (8 floats per lane)
 
     float A2[kH], Ai[kH], An[kH];
     float min_a2, dvec;
@@ -152,7 +153,7 @@ struct Bwd {
     __device__ Bwd(const BwdCols& c_, const BwdShape& s, int64_t b_, int64_t d_raw, float4* lds_)
         : c(c_), L(s.L), D(s.D), N(NS > 0 ? NS : s.N), b(b_),
           d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)), live(d_raw < s.D),
-          half(threadIdx.x >> 5), gated(c_.z != nullptr), lds(lds_) {}
+          half(threadIdx.x >> 5), gated(c_.z != nullptr), lds(lds_), acache(lds_ + kWave) {}
 
     __device__ __forceinline__ bool valid(int j) const {
         return NS > 0 || static_cast<int>(half) * kH + j < N;
@@ -217,9 +218,10 @@ struct Bwd {
     // absolute error that would compound over a long memory.
     template <bool SLOW>
     __device__ __forceinline__ void fwd_state(int j, float& h, float uv, float dv, float dvu,
-                                              float Bj) const {
+                                              float Bj, float& aout) const {
         const float x2 = dv * A2[j];
         const float a = ex2(x2);
+        aout = a;
         if constexpr (!SLOW) {
             if constexpr (kZoh) {
                 const float k = (uv * Ai[j]) * Bj;
@@ -245,17 +247,19 @@ struct Bwd {
         return SM == kAll || (SM == kFirst && j == 0);
     }
 
+    // av: the step's aBar per state (0 for padding states).
     template <int SM>
-    __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv,
-                                        const float (&Bv)[kH]) const {
+    __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv, const float (&Bv)[kH],
+                                        float (&av)[kH]) const {
         const float dvu = dv * uv;
 #pragma unroll
         for (int j = 0; j < kH; j++) {
+            av[j] = 0.0f;
             if (!valid(j)) continue;
             if (slow_state<SM>(j))
-                fwd_state<true>(j, h[j], uv, dv, dvu, Bv[j]);
+                fwd_state<true>(j, h[j], uv, dv, dvu, Bv[j], av[j]);
             else
-                fwd_state<false>(j, h[j], uv, dv, dvu, Bv[j]);
+                fwd_state<false>(j, h[j], uv, dv, dvu, Bv[j], av[j]);
         }
     }
 
@@ -271,12 +275,15 @@ struct Bwd {
     // dh + m dh, and for ZOH the dA term as dv aBar h_{t-1} + K t5 with
     // t5 = dv aBar - q from its series dv x (1/2 + x/3 + x^2/8 + x^3/30)
     // (x = dv A) where |x| < 2^-6: the direct difference cancels there.
+    // FULL steps take aBar from the block's recompute (a_in); the replay
+    // computes it.
     template <bool SLOW, bool FULL>
     __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float uv,
                                               float dv, float udv, float dY, float Bj, float Cj,
-                                              float& du_acc, float& ddv_acc, float& dBp) const {
-        const float x2 = dv * A2[j];
-        const float a = ex2(x2);
+                                              float a_in, float& du_acc, float& ddv_acc,
+                                              float& dBp) const {
+        const float x2 = (SLOW || !FULL) ? dv * A2[j] : 0.0f;
+        const float a = FULL ? a_in : ex2(x2);
         const float dh = __builtin_fmaf(Cj, dY, g);
         float m = 0.0f, gn;
         if constexpr (SLOW) {
@@ -322,8 +329,8 @@ struct Bwd {
     template <int SM, bool FULL>
     __device__ __forceinline__ void rev(float (&g)[kH], float (&dA)[kH], const float (&hp)[kH],
                                         float uv, float dv, float dY, const float (&Bv)[kH],
-                                        const float (&Cv)[kH], float& du_acc, float& ddv_acc,
-                                        float (&dBp)[kH]) const {
+                                        const float (&Cv)[kH], const float (&av)[kH],
+                                        float& du_acc, float& ddv_acc, float (&dBp)[kH]) const {
         const float udv = uv * dv;
 #pragma unroll
         for (int j = 0; j < kH; j++) {
@@ -333,10 +340,10 @@ struct Bwd {
             }
             if (slow_state<SM>(j))
                 rev_state<true, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
-                                      du_acc, ddv_acc, dBp[j]);
+                                      av[j], du_acc, ddv_acc, dBp[j]);
             else
                 rev_state<false, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
-                                       du_acc, ddv_acc, dBp[j]);
+                                       av[j], du_acc, ddv_acc, dBp[j]);
         }
     }
 
@@ -446,9 +453,9 @@ struct Bwd {
 #pragma unroll
         for (int i = 0; i < kT; i++) {
             if (i >= n) break;
-            float Bv[kH];
+            float Bv[kH], av[kH];
             read_row(0, i, Bv);
-            fwd<SM>(h, uu[i], dv[i], Bv);
+            fwd<SM>(h, uu[i], dv[i], Bv, av);
         }
     }
 
@@ -456,13 +463,14 @@ struct Bwd {
     template <int SM>
     __device__ __forceinline__ void rev_block(float (&g)[kH], const float (&dv)[kT],
                                               const float (&dY)[kT], int n) const {
-        float dA[kH] = {}, hp[kH] = {}, dBp[kH], Bv[kH] = {}, du_acc = 0.0f, ddv_acc = 0.0f;
+        float dA[kH] = {}, hp[kH] = {}, dBp[kH], Bv[kH] = {}, av[kH] = {}, du_acc = 0.0f,
+              ddv_acc = 0.0f;
 #pragma unroll
         for (int i = kT - 1; i >= 0; i--) {
             if (i >= n) continue;
             float Cv[kH];
             read_row(32, i, Cv);
-            rev<SM, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+            rev<SM, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
         }
     }
 
@@ -513,10 +521,13 @@ struct Bwd {
 #pragma unroll
         for (int i = 0; i < kT; i++) {
             if (i >= n) break;
-            float Bv[kH], Cv[kH];
+            float Bv[kH], Cv[kH], av[kH];
             read_row(0, i, Bv);
             read_row(32, i, Cv);
-            fwd<SM>(h, uu[i], dv[i], Bv);
+            fwd<SM>(h, uu[i], dv[i], Bv, av);
+            // aBar of the step, kept for the adjoint below (this lane only)
+            acache[(i * kWave + threadIdx.x) * 2] = make_float4(av[0], av[1], av[2], av[3]);
+            acache[(i * kWave + threadIdx.x) * 2 + 1] = make_float4(av[4], av[5], av[6], av[7]);
             if (i + 1 < kT) {
 #pragma unroll
                 for (int j = 0; j < kH; j++) hist[i + 1][j] = h[j];
@@ -541,8 +552,11 @@ struct Bwd {
             float Bv[kH], Cv[kH], dBp[kH];
             read_row(0, i, Bv);
             read_row(32, i, Cv);
+            const float4 a_lo = acache[(i * kWave + threadIdx.x) * 2];
+            const float4 a_hi = acache[(i * kWave + threadIdx.x) * 2 + 1];
+            const float av[kH] = {a_lo.x, a_lo.y, a_lo.z, a_lo.w, a_hi.x, a_hi.y, a_hi.z, a_hi.w};
             float du_acc = 0.0f, ddv_acc = 0.0f;
-            rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, du_acc, ddv_acc, dBp);
+            rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
             const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
             const float ddv = pair_sum(ddv_acc);
             const int64_t r = row(s + i);
@@ -560,7 +574,7 @@ struct Bwd {
 template <int DISC, int NS>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_bwd_kernel(
     BwdCols c, BwdShape s) {
-    __shared__ float4 lds[kWave];
+    __shared__ float4 lds[kWave + kT * kWave * 2];   // B/C staging, then the aBar cache
     const int64_t w = blockIdx.x;
     const int64_t ti = w / s.nseg;
     const int64_t sg = w - ti * s.nseg;
