@@ -143,7 +143,7 @@ int cu_count() {
 }
 
 mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const float* B,
-                          const float* C) {
+                          const float* C, const float* z) {
     static const int64_t waves_per_cu = env_or("MSS_SCAN_WAVES_PER_CU", 8);
     static const int64_t min_seg = env_or("MSS_SCAN_MIN_SEG", 512);
     mss::ScanShape s;
@@ -166,8 +166,9 @@ mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const flo
     s.ld_y = ld.y;
     s.bc_vec = reinterpret_cast<uintptr_t>(B) % 16 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
                ld.B % 4 == 0 && ld.C % 4 == 0;
-    s.dense = ld.x == s.D && ld.z == s.D && ld.delta == s.D && ld.y == s.D && ld.B == s.N &&
-              ld.C == s.N;
+    // (the z stride matters only when z is given)
+    s.dense = ld.x == s.D && (z == nullptr || ld.z == s.D) && ld.delta == s.D && ld.y == s.D &&
+              ld.B == s.N && ld.C == s.N;
     return s;
 }
 
@@ -237,7 +238,7 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
     }
     const mss::ScanArgs a{disc, fused, src, delta, A_log, B, C, D_vec, z, h0, w_conv, b_conv,
                           y, h_cache, h_last};
-    const hipError_t e = mss::launch_scan(a, scan_shape(dims, ld, B, C), stream);
+    const hipError_t e = mss::launch_scan(a, scan_shape(dims, ld, B, C, z), stream);
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
