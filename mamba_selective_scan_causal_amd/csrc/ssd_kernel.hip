@@ -229,8 +229,10 @@ struct Ssd {
         }
     }
 
-    // y for the chunk (rows < nout are written) from G X + (e^c C) S + D x.
-    // The two 16-row tiles run interleaved (independent accumulation chains).
+    // y for the chunk (rows < nout are written) = G X + diag(2^c) (C S) + D x.
+    // The two 16-row tiles run interleaved (independent accumulation chains);
+    // C S accumulates apart from G X so that its row scale 2^{c_i} is applied
+    // once to the finished tile instead of to every operand.
     __device__ __forceinline__ void output(const v4f (&S)[C_::CTW][C_::NT], int64_t t0,
                                            int nout) const {
         const float* G = lds + C_::oG;
@@ -238,12 +240,17 @@ struct Ssd {
         const float* Cc = lds + C_::oC;
         const float* cum = lds + C_::oCum;
         const int64_t HP = a.H * P;
-        const float f0 = ex2(cum[q16]), f1 = ex2(cum[16 + q16]);
+        float f0[4], f1[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            f0[r] = ex2(cum[4 * g4 + r]);
+            f1[r] = ex2(cum[16 + 4 * g4 + r]);
+        }
 #pragma unroll
         for (int c = 0; c < C_::CTW; c++) {
             const int ct = wave * C_::CTW + c;
             if (ct >= C_::CT) break;
-            v4f y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
+            v4f y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, o0 = y0, o1 = y0;
             const float* G0 = G + q16 * C_::LDQ + 4 * g4;
             const float* G1 = G0 + 16 * C_::LDQ;
             const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
@@ -267,14 +274,14 @@ struct Ssd {
             for (int tn = 0; tn < C_::NT; tn++) {
                 const float4 c0 = *reinterpret_cast<const float4*>(C0 + 16 * tn);
                 const float4 c1 = *reinterpret_cast<const float4*>(C1 + 16 * tn);
-                y0 = mfma(c0.x * f0, S[c][tn][0], y0);
-                y1 = mfma(c1.x * f1, S[c][tn][0], y1);
-                y0 = mfma(c0.y * f0, S[c][tn][1], y0);
-                y1 = mfma(c1.y * f1, S[c][tn][1], y1);
-                y0 = mfma(c0.z * f0, S[c][tn][2], y0);
-                y1 = mfma(c1.z * f1, S[c][tn][2], y1);
-                y0 = mfma(c0.w * f0, S[c][tn][3], y0);
-                y1 = mfma(c1.w * f1, S[c][tn][3], y1);
+                o0 = mfma(c0.x, S[c][tn][0], o0);
+                o1 = mfma(c1.x, S[c][tn][0], o1);
+                o0 = mfma(c0.y, S[c][tn][1], o0);
+                o1 = mfma(c1.y, S[c][tn][1], o1);
+                o0 = mfma(c0.z, S[c][tn][2], o0);
+                o1 = mfma(c1.z, S[c][tn][2], o1);
+                o0 = mfma(c0.w, S[c][tn][3], o0);
+                o1 = mfma(c1.w, S[c][tn][3], o1);
             }
             const int p = 16 * ct + q16;
             // x of rows 4 g4 .. 4 g4 + 3 (and 16 more) of column p: one
@@ -286,9 +293,11 @@ struct Ssd {
             for (int r = 0; r < 4; r++) {
                 const int i0 = 4 * g4 + r, i1 = 16 + 4 * g4 + r;
                 if (i0 < nout)
-                    a.y[row(t0 + i0) * HP + h * P + p] = __builtin_fmaf(dskip, xs0[r], y0[r]);
+                    a.y[row(t0 + i0) * HP + h * P + p] =
+                        __builtin_fmaf(dskip, xs0[r], __builtin_fmaf(f0[r], o0[r], y0[r]));
                 if (i1 < nout)
-                    a.y[row(t0 + i1) * HP + h * P + p] = __builtin_fmaf(dskip, xs1[r], y1[r]);
+                    a.y[row(t0 + i1) * HP + h * P + p] =
+                        __builtin_fmaf(dskip, xs1[r], __builtin_fmaf(f1[r], o1[r], y1[r]));
             }
         }
     }
