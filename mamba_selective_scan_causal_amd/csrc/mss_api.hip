@@ -583,10 +583,11 @@ int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float
         const hipError_t e = mss::launch_state_init(h0, h_last, BHPN, stream);
         return e == hipSuccess ? MSS_OK : hip_fail(e);
     }
-    // Segments: about four workgroups per CU, none shorter than
-    // MSS_SSD_MIN_SEG steps (default 512), so that the replay that rebuilds a
-    // segment's initial state stays a small share of its work.
-    static const int64_t wg_per_cu = env_or("MSS_SSD_WG_PER_CU", 4);
+    // Segments: about five workgroups per CU (two are resident at a time;
+    // the surplus evens out the finish), none shorter than MSS_SSD_MIN_SEG
+    // steps (default 512), so that the replay that rebuilds a segment's
+    // initial state stays a small share of its work.
+    static const int64_t wg_per_cu = env_or("MSS_SSD_WG_PER_CU", 5);
     static const int64_t min_seg = env_or("MSS_SSD_MIN_SEG", 512);
     const int64_t Q = mss::ssd_chunk_len();
     const int64_t nchunks = (L + Q - 1) / Q;
