@@ -106,7 +106,28 @@ def _time_ms(fn, stream, reps, warm=2):
     return a.elapsed_time(b) / reps
 
 
-def extras(w, d, y, disc, stream, with_oracle=True):
+def _event_times(fn, stream, reps, before=None):
+    """Per-call hipEvent times of fn() on `stream` (ms); before() runs ahead
+    of each call, outside the timed interval."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _stats(ts):
+    return {"mean": float(np.mean(ts)), "median": float(np.median(ts)), "min": float(np.min(ts)),
+            "calls": len(ts)}
+
+
+def extras(w, inp, d, y, disc, stream, with_oracle=True):
     """Side measurements: the other discretisation, the unfused path (conv
     kernel, then the scan on u), and the decode workload (256 sequences x
     5120 channels, 64 consecutive single-token steps)."""
@@ -120,15 +141,25 @@ def extras(w, d, y, disc, stream, with_oracle=True):
                                          d["B"], d["C"], d["D_vec"], d["z"], None, disc=other,
                                          **kw), stream, 10)
     res[f"fused_{other}_ms"] = t
+    # cold: a 512 MB buffer is written between calls, so that the inputs are
+    # not served from the 256 MB last-level cache
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = _event_times(lambda: mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"],
+                                                d["A_log"], d["B"], d["C"], d["D_vec"], d["z"],
+                                                None, disc=disc, **kw),
+                        stream, 10, before=lambda: flush.fill_(1.0))
+    res["fused_cold_ms"] = _stats(cold)
     u = torch.empty_like(d["x"])
     tc = _time_ms(lambda: mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch,
                                           seq_len=w.seq_len, out=u, stream=stream), stream, 10)
-    ts = _time_ms(lambda: mss.selective_scan(u, d["delta"], d["A_log"], d["B"], d["C"],
-                                             d["D_vec"], d["z"], None, disc=disc, **kw),
-                  stream, 10)
+    ts = {m: _time_ms(lambda: mss.selective_scan(u, d["delta"], d["A_log"], d["B"], d["C"],
+                                                 d["D_vec"], d["z"], None, disc=m, **kw),
+                      stream, 10)
+          for m in (disc, other)}
     MD = w.M * w.d_inner
     res["unfused"] = {"conv1d_silu_ms": tc, "conv1d_silu_GBps": 8 * MD / tc / 1e6,
-                      "scan_on_u_ms": ts, "total_ms": tc + ts}
+                      "scan_on_u_ms": ts[disc], f"scan_on_u_{other}_ms": ts[other],
+                      "total_ms": tc + ts[disc]}
     del u
     dw = gen.DECODE
     dinp = gen.generate(dw)
@@ -143,6 +174,14 @@ def extras(w, d, y, disc, stream, with_oracle=True):
                                stream=stream)
 
     t64 = _time_ms(decode64, stream, 3, warm=1)
+
+    def one_step():
+        mss.selective_step(dd["x"][0], dd["z"][0], dd["delta"][0], dd["A_log"], dd["B"][0],
+                           dd["C"][0], dd["D_vec"], dd["w_conv"], dd["b_conv"],
+                           dd["conv_state"], dd["h"], disc=disc, out=yd, stream=stream)
+
+    step_cold = _event_times(one_step, stream, 16, before=lambda: flush.fill_(1.0))
+    del flush
     res["backward"] = backward_extras(w, d, stream, with_oracle=with_oracle)
     res["ssd"] = ssd_extras(stream, with_oracle=with_oracle)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
@@ -150,7 +189,11 @@ def extras(w, d, y, disc, stream, with_oracle=True):
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
                      "algorithmic_bytes_per_step": step_bytes,
                      "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
-                     "note": "h + conv window (~100 MB) fit the 256 MB last-level cache"}
+                     "note": "h + conv window (~100 MB) fit the 256 MB last-level cache",
+                     "cold_us_per_step": _stats([t * 1e3 for t in step_cold]),
+                     "cold_GBps": step_bytes / float(np.median(step_cold)) / 1e6}
+    if with_oracle:
+        res["cpu_oracle_1core"] = cpu_baseline(w, inp, disc, target_s=4.0, threads=1)
     return res
 
 
@@ -279,11 +322,11 @@ def ssd_oracle_rate(w, inp, heads=4):
                       f"fp64 C, {t:.1f} s"}
 
 
-def cpu_baseline(w, inp, disc, target_s=15.0):
+def cpu_baseline(w, inp, disc, target_s=15.0, threads=None):
     """The oracle as it stands, on a bounded sample of whole (b, d) columns of
-    the same workload, on all host cores it may use."""
+    the same workload, on all host cores it may use (or on `threads`)."""
     import oracle
-    cores = len(os.sched_getaffinity(0))
+    cores = threads or len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
     allcols = w.batch * w.d_inner
 
@@ -367,7 +410,8 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_times = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(kern_times))
     ms_per_step = wall * 1e3 / args.steps
     elems = w.M * w.d_inner
     value = elems / (ms_per_step / 1e3)
@@ -403,9 +447,11 @@ def main():
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": abytes},
                      "kernel_digest": digest},
+        "kernel_ms": _stats(kern_times),
     }
     if not args.no_extras:
-        out["extra"] = extras(w, d, y, args.disc, stream, with_oracle=not args.no_cpu_baseline)
+        out["extra"] = extras(w, inp, d, y, args.disc, stream,
+                              with_oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.disc)
     print(json.dumps(out), flush=True)
