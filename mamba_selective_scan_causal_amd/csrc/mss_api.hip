@@ -197,9 +197,9 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
     const mss_strides ld = strided ? *strides : dense_strides(dims);
     const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
     const int64_t K = dims->d_conv;
-    int64_t M, MD, MN, DN, BDN, BLDN;
+    int64_t M, MD, MN, DN, DK, BDN, BLDN;
     if (!count(M, {Bt, L}) || !count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) ||
-        !count(DN, {D, N}) || !count(BDN, {Bt, D, N}) ||
+        !count(DN, {D, N}) || !count(DK, {D, K}) || !count(BDN, {Bt, D, N}) ||
         (h_cache && !count(BLDN, {Bt, L, D, N})))
         return MSS_EINVAL;
     if (!h_cache) BLDN = 0;
@@ -220,7 +220,7 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
         ck.out(y, MD, true);
     }
     if (fused) {
-        ck.in(w_conv, D * K, true);
+        ck.in(w_conv, DK, true);
         ck.in(b_conv, D, false);
     }
     ck.in(A_log, DN, true);
@@ -432,15 +432,15 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
     int st = check_dims(dims, true, true);
     if (st != MSS_OK) return st;
     const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, K = dims->d_conv;
-    int64_t MD;
-    if (!count(MD, {Bt, L, D})) return MSS_EINVAL;
+    int64_t MD, DK;
+    if (!count(MD, {Bt, L, D}) || !count(DK, {D, K})) return MSS_EINVAL;
     Checker ck;
     ck.in(x, MD, true);
-    ck.in(w_conv, D * K, true);
+    ck.in(w_conv, DK, true);
     ck.in(b_conv, D, false);
     ck.in(du, MD, true);
     ck.out(dx, MD, true);
-    ck.out(dw_conv, D * K, true);
+    ck.out(dw_conv, DK, true);
     ck.out(db_conv, D, false);
     const int64_t need = MD > 0 ? conv_bwd_bytes(dims) : 0;
     if (MD > 0 && ((D + 63) / 64) * conv_bwd_groups(dims) > INT32_MAX) return MSS_EINVAL;
@@ -450,7 +450,7 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
     st = check_workspace(workspace, workspace_bytes, need);
     if (st != MSS_OK) return st;
     if (MD == 0) {
-        if ((st = zero_fill(dw_conv, D * K, stream)) != MSS_OK) return st;
+        if ((st = zero_fill(dw_conv, DK, stream)) != MSS_OK) return st;
         return zero_fill(db_conv, D, stream);
     }
     const mss::ConvBwdArgs a{Bt, L, D, static_cast<int>(K), conv_bwd_groups(dims), x, w_conv,
@@ -465,11 +465,11 @@ int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv, c
     int st = check_dims(dims, true, true);
     if (st != MSS_OK) return st;
     const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, K = dims->d_conv;
-    int64_t MD;
-    if (!count(MD, {Bt, L, D})) return MSS_EINVAL;
+    int64_t MD, DK;
+    if (!count(MD, {Bt, L, D}) || !count(DK, {D, K})) return MSS_EINVAL;
     Checker ck;
     ck.in(x, MD, true);
-    ck.in(w_conv, D * K, true);
+    ck.in(w_conv, DK, true);
     ck.in(b_conv, D, false);
     ck.out(u, MD, true);
     st = ck.finish();
@@ -523,9 +523,9 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
     if (st != MSS_OK) return st;
     if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
     const int64_t Bt = dims->batch, D = dims->d_inner, N = dims->d_state, K = dims->d_conv;
-    int64_t BD, BN, DN, BDN, BKD;
+    int64_t BD, BN, DN, DK, BDN, BKD;
     if (!count(BD, {Bt, D}) || !count(BN, {Bt, N}) || !count(DN, {D, N}) ||
-        !count(BDN, {Bt, D, N}) || !count(BKD, {Bt, K - 1, D}))
+        !count(DK, {D, K}) || !count(BDN, {Bt, D, N}) || !count(BKD, {Bt, K - 1, D}))
         return MSS_EINVAL;
     Checker ck;
     ck.in(x, BD, true);
@@ -535,7 +535,7 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
     ck.in(B, BN, true);
     ck.in(C, BN, true);
     ck.in(D_vec, D, false);
-    ck.in(w_conv, D * K, true);
+    ck.in(w_conv, DK, true);
     ck.in(b_conv, D, false);
     ck.out(conv_state, BKD, true);
     ck.out(h, BDN, true);

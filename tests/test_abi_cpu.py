@@ -129,6 +129,15 @@ def test_core_and_conv_validation(L):
     assert L.mss_mamba1_core(ctypes.byref(d), 0, *args, None) == EINVAL
     d0 = mss.make_dims(2, 16, 64, 16, 0)  # K = 0
     assert L.mss_mamba1_core(ctypes.byref(d0), 0, *[fake(i) for i in range(1, 14)], None) == EINVAL
+    # an empty sequence does not excuse a d_inner whose (D, K) conv weight
+    # size overflows
+    wide = mss.make_dims(1, 0, 1 << 62, 1, 4)
+    assert L.mss_conv1d_silu(ctypes.byref(wide), fake(1), fake(2), None, fake(3), None) == EINVAL
+    assert L.mss_mamba1_core(ctypes.byref(wide), 0, *[fake(i) for i in range(1, 14)],
+                             None) == EINVAL
+    assert L.mss_selective_step(ctypes.byref(mss.make_dims(0, 1, 1 << 62, 1, 4)), 0,
+                                *[fake(i) for i in range(1, 13)], None) == EINVAL
+    assert conv_bwd_call(L, wide, ws_size=0) == EINVAL
 
 
 def test_step_validation(L):
