@@ -146,6 +146,7 @@ def _ptr(t, name, shape, required=True):
         raise TypeError(f"{name} must be float32, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
+    _same_device(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if tuple(t.shape) != tuple(shape):
@@ -163,12 +164,20 @@ def _rows(t, name, rows, cols, required=True):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
         raise TypeError(f"{name} must be a float32 GPU tensor")
+    _same_device(t, name)
     if tuple(t.shape) != (rows, cols):
         raise ValueError(f"{name}: expected shape {(rows, cols)}, got {tuple(t.shape)}")
     if rows > 0 and cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name}: columns must be contiguous")
     ld = t.stride(0) if rows > 1 else cols
     return (t.data_ptr() or None), ld
+
+
+def _same_device(t, name):
+    # the kernels run on the current device: every tensor must live there
+    dev = _torch().cuda.current_device()
+    if t.device.index != dev:
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{dev}")
 
 
 def _dense(*ts):
@@ -178,6 +187,9 @@ def _dense(*ts):
 def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {s.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -321,6 +333,7 @@ def _workspace(op, like, workspace, stream, **dims):
             workspace.record_stream(stream)
     if workspace.dtype != _torch().uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    _same_device(workspace, "workspace")
     base = workspace.data_ptr()
     pad = (-base) % 256
     return base + pad, max(0, workspace.numel() - pad), workspace
