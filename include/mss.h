@@ -97,7 +97,7 @@ int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv,
  *   Optional (NULL allowed): D_vec (= 0), z (ungated output), h0 (= 0),
  *   h_cache, h_last.  Required: u, delta, A_log, B, C, y.
  *   The carried state between time segments processed in parallel drops
- *   contributions that have decayed by more than 2^-30 (see the design
+ *   contributions that have decayed by more than 2^-24 (see the design
  *   notes); the result is otherwise the plain recurrence in fp32.          */
 int mss_selective_scan(const mss_dims* dims, int disc, const float* u, const float* delta,
                        const float* A_log, const float* B, const float* C, const float* D_vec,
@@ -197,7 +197,7 @@ int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes);
  *   dz (M, D)      = dout y SiLU'(z), y ungated     (required iff z given)
  *   dh0 (B, D, N)  = the adjoint after step 0       (NULL: not computed)
  * The adjoint carried between time segments processed in parallel drops
- * contributions that have decayed by more than 2^-30, as in the forward.  */
+ * contributions that have decayed by more than 2^-24, as in the forward.  */
 int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 const float* delta, const float* A_log, const float* B,
                                 const float* C, const float* D_vec, const float* z,
@@ -228,7 +228,7 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
  * with f = dv (MSS_DISC_EULER, the Mamba-2 form) or expm1(dv A_h) / A_h
  * (MSS_DISC_ZOH, the discretisation of the pages' Mamba-1 path).
  * Computed in chunks on the matrix cores (fp32 MFMA); segments processed in
- * parallel drop contributions that have decayed by more than 2^-30. */
+ * parallel drop contributions that have decayed by more than 2^-24. */
 typedef struct mss_ssd_dims {
     int32_t struct_size;    /* sizeof(mss_ssd_dims) */
     int32_t reserved;       /* must be 0 */

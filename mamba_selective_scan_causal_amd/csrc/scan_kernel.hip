@@ -25,10 +25,11 @@
 // h(t0 - 1).  Because the recurrence forgets exponentially -- the part of
 // h(t0-1) that comes from before step s is multiplied by
 // prod_{r=s}^{t0-1} aBar_r = exp(A_n * sum_r dv_r) -- the wave first walks
-// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= 30 ln 2 holds in
+// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= 24 ln 2 holds in
 // every lane (or t = 0 is reached), then replays the recurrence forward from
 // that step with h = 0 (state only, no outputs).  What this drops is exactly
-// the state at the replay start times a factor <= 2^-30 per state; reaching
+// the state at the replay start times a factor <= 2^-24 per state (the unit
+// roundoff of fp32: below one rounding of the state it came from); reaching
 // t = 0 makes it exact.  No workspace and no inter-wave synchronisation.
 #include "device_math.h"
 #include "launch.h"
@@ -38,7 +39,7 @@ namespace {
 
 constexpr int kT = 8;                         // steps per straight-line block
 constexpr int kBackBlk = 16;                  // delta loads in flight in the backward walk
-constexpr float kDecayCut = 30.0f;            // replay until the carried part decays by 2^-30
+constexpr float kDecayCut = 24.0f;            // replay until the carried part decays by 2^-24
 // Below |dv*A| = 2^-6 the decay is applied through expm1 (see step()).
 constexpr float kSmallX = 0.015625f;
 constexpr float kSmallX2 = kSmallX * kLog2e;  // the same bound in log2 units
