@@ -295,8 +295,11 @@ struct Bwd {
         g = gn;
         if constexpr (FULL) {
             if constexpr (kZoh) {
-                if constexpr (!SLOW) m = a - 1.0f;
-                const float q = m * Ai[j];
+                // q = (aBar - 1) / A: one fma on the fast path, where
+                // |dv A| >= 2^-6 keeps aBar - 1 away from cancellation
+                float q;
+                if constexpr (!SLOW) q = __builtin_fmaf(a, Ai[j], -Ai[j]);
+                else q = m * Ai[j];
                 const float dq = dh * q;
                 du_acc = __builtin_fmaf(dq, Bj, du_acc);
                 dBp = dq * uv;
