@@ -175,6 +175,25 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
 
     t64 = _time_ms(decode64, stream, 3, warm=1)
 
+    # the same 64 steps captured once as a HIP graph and replayed
+    def decode64_current():
+        for s_ in range(dw.seq_len):
+            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
+                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
+                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode64_current()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode64_current()
+    t64g = _time_ms(graph.replay, torch.cuda.current_stream(), 3, warm=1)
+    del graph
+
     def one_step():
         mss.selective_step(dd["x"][0], dd["z"][0], dd["delta"][0], dd["A_log"], dd["B"][0],
                            dd["C"][0], dd["D_vec"], dd["w_conv"], dd["b_conv"],
@@ -190,6 +209,7 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
                      "algorithmic_bytes_per_step": step_bytes,
                      "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
                      "note": "h + conv window (~100 MB) fit the 256 MB last-level cache",
+                     "graph_us_per_step": t64g * 1e3 / dw.seq_len,
                      "cold_us_per_step": _stats([t * 1e3 for t in step_cold]),
                      "cold_GBps": step_bytes / float(np.median(step_cold)) / 1e6}
     if with_oracle:
