@@ -141,6 +141,14 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
                                          d["B"], d["C"], d["D_vec"], d["z"], None, disc=other,
                                          **kw), stream, 10)
     res[f"fused_{other}_ms"] = t
+    # a plain 1 GiB device copy (read + write) for scale: the HBM rate a
+    # simple streaming kernel reaches on this part
+    src = torch.ones(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    tcopy = _time_ms(lambda: dst.copy_(src), stream, 10)
+    res["copy_1GiB"] = {"ms": tcopy, "GBps": 2 * COPY_BYTES / tcopy / 1e6,
+                        "frac_of_peak": 2 * COPY_BYTES / tcopy / 1e6 / HBM_PEAK_GBS}
+    del src, dst
     # cold: a 512 MB buffer is written between calls, so that the inputs are
     # not served from the 256 MB last-level cache
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
@@ -202,7 +210,7 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
     step_cold = _event_times(one_step, stream, 16, before=lambda: flush.fill_(1.0))
     del flush
     res["backward"] = backward_extras(w, d, stream, with_oracle=with_oracle)
-    res["ssd"] = ssd_extras(stream, with_oracle=with_oracle)
+    res["ssd"] = ssd_extras(stream, reps=10, with_oracle=with_oracle)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
     step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
