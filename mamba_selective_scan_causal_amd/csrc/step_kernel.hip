@@ -6,10 +6,14 @@
 // caller-owned buffers that are updated in place.
 //
 // HBM-bound: per (b, d) it reads and writes h (2 * 4N bytes) and the conv
-// window (2 * 4(K-1) bytes) plus x, z, delta, y.  Lane = channel d: the N
-// states of a lane are contiguous, so a wave moves 64 * 4N contiguous bytes
-// with 16-byte vector accesses; B and C rows of a batch entry are
-// wave-uniform scalar loads.
+// window (2 * 4(K-1) bytes) plus x, z, delta, y.  A lane owns one channel and
+// its N states, so a wave's h block (64 channels) is 64 * 4N contiguous
+// bytes.  With N = 16 that block moves in 16-byte pieces with consecutive
+// lanes on consecutive pieces (each access one contiguous 1 KB): piece i of
+// lane (m, s) = (lane / 4, lane % 4) holds states 4 s .. 4 s + 3 of channel
+// 16 i + m, so lane (m, s) is given channel 16 s + m, and a 4 x 4 transpose
+// of the pieces inside each quad of lanes (DPP) puts a channel's 16 states
+// in its lane.  B and C rows of a batch entry are wave-uniform.
 #include "device_math.h"
 #include "launch.h"
 
@@ -22,6 +26,40 @@ constexpr float kSmallX = 0.015625f;          // same ZOH expm1 switch as the sc
 // loaded and transformed once for kRows rows, and all loads of the rows are
 // issued before any arithmetic so that their latencies overlap.
 constexpr int kRows = 2;
+
+// The value of lane ^ B (B = 1 or 2) inside its quad (DPP quad_perm).
+template <int B>
+__device__ __forceinline__ float quad_xor(float v) {
+    constexpr int ctrl = B == 1 ? 0xb1 : 0x4e;   // [1,0,3,2] or [2,3,0,1]
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true));
+}
+
+// One level of the in-quad transpose of v[piece][component]: the lanes whose
+// bit B is clear keep pieces without bit B and trade the others with lane ^ B.
+template <int B>
+__device__ __forceinline__ void quad_trade(float (&v)[4][4]) {
+    const bool hi = (threadIdx.x & B) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (i & B) continue;
+        const int j = i | B;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float recv = quad_xor<B>(hi ? v[i][k] : v[j][k]);
+            if (hi)
+                v[i][k] = recv;
+            else
+                v[j][k] = recv;
+        }
+    }
+}
+
+// Lane g of a quad ends with piece i = lane i's piece g (its own inverse).
+__device__ __forceinline__ void quad_transpose(float (&v)[4][4]) {
+    quad_trade<1>(v);
+    quad_trade<2>(v);
+}
 
 template <int DISC, int KS, int NS>
 __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
@@ -36,7 +74,10 @@ __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
     const int64_t nblk = groups * tiles;
     for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
         const int64_t g = blk / tiles;
-        const int64_t d_raw = (blk - g * tiles) * kWave + threadIdx.x;
+        const int64_t d0 = (blk - g * tiles) * kWave;   // first channel of the tile
+        // N = 16: lane (m, s) owns channel 16 s + m (see the file header)
+        const int64_t d_raw =
+            d0 + (kStageBC ? 16 * (threadIdx.x & 3u) + (threadIdx.x >> 2) : threadIdx.x);
         const bool valid = d_raw < a.D;
         const int64_t d = valid ? d_raw : a.D - 1;
         int64_t bs[kRows];
@@ -70,14 +111,32 @@ __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
             for (int k = 1; k < KR; k++)
                 prev[r][k - 1] =
                     k < K ? a.conv_state[(bs[r] * (K - 1) + (K - 1 - k)) * a.D + d] : 0.0f;
-            const float* hp = a.h + bd * N;
-            if constexpr (NS > 0 && NS % 4 == 0) {
+            if constexpr (kStageBC) {
+                // piece q = 64 i + lane of the row's block: channel d0 + q / 4
+                const float4* src =
+                    reinterpret_cast<const float4*>(a.h + (bs[r] * a.D + d0) * 16);
+                float v[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int q = i * kWave + static_cast<int>(threadIdx.x);
+                    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (d0 + q / 4 < a.D) t = src[q];
+                    v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
+                }
+                quad_transpose(v);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int k = 0; k < 4; k++) h[r][4 * i + k] = v[i][k];
+            } else if constexpr (NS > 0 && NS % 4 == 0) {
+                const float* hp = a.h + bd * N;
 #pragma unroll
                 for (int n = 0; n < NR; n += 4) {
                     const float4 v = *reinterpret_cast<const float4*>(hp + n);
                     h[r][n] = v.x; h[r][n + 1] = v.y; h[r][n + 2] = v.z; h[r][n + 3] = v.w;
                 }
             } else {
+                const float* hp = a.h + bd * N;
 #pragma unroll
                 for (int n = 0; n < NR; n++) h[r][n] = n < N ? hp[n] : 0.0f;
             }
@@ -155,11 +214,29 @@ __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
                     yv = __builtin_fmaf(Cv[r][n], h[r][n], yv);
                 }
             }
+            if constexpr (kStageBC) {
+                // back to pieces (every lane of the quad takes part), then
+                // one contiguous 1 KB store per piece index
+                float v[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int k = 0; k < 4; k++) v[i][k] = h[r][4 * i + k];
+                quad_transpose(v);
+                float4* dst = reinterpret_cast<float4*>(a.h + (bs[r] * a.D + d0) * 16);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int q = i * kWave + static_cast<int>(threadIdx.x);
+                    if (d0 + q / 4 < a.D) dst[q] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+                }
+            }
             if (valid) {
                 const int64_t bd = bs[r] * a.D + d;
                 a.y[bd] = a.z ? yv * silu(zv[r]) : yv;
                 float* hp = a.h + bd * N;
-                if constexpr (NS > 0 && NS % 4 == 0) {
+                if constexpr (kStageBC) {
+                    // stored above
+                } else if constexpr (NS > 0 && NS % 4 == 0) {
 #pragma unroll
                     for (int n = 0; n < NR; n += 4)
                         *reinterpret_cast<float4*>(hp + n) =
