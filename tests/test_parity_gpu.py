@@ -127,6 +127,39 @@ def test_core_2p8b_width_sampled(disc):
                  "h_last (sampled)")
 
 
+def test_hcache_beyond_2_31_elements():
+    """hCache of 1 x 4200 x 32768 x 16 = 2.2e9 elements (8.8 GB): offsets
+    past 2^31 in the state cache (and D = 32768: 512 channel tiles).  y and
+    the whole hCache column of sampled channels against the oracle; the last
+    hCache row equals h_last bitwise."""
+    import torch
+    w = gen.MAMBA_2P8B.with_(name="hcache_2e9", batch=1, seq_len=4200, d_inner=32768,
+                             hcache=True, seed_index=31)
+    B, L, D, N = w.batch, w.seq_len, w.d_inner, w.d_state
+    assert B * L * D * N > 2 ** 31
+    inp = gen.generate(w)
+    d = {k: dev(v) for k, v in inp.items()}
+    y = torch.empty((B * L, D), device="cuda")
+    hc = torch.empty((B, L, D, N), device="cuda")
+    hl = torch.empty((B, D, N), device="cuda")
+    mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                    d["D_vec"], d["z"], None, batch=B, seq_len=L, disc="zoh", h_cache=hc,
+                    h_last=hl, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(hc[:, L - 1], hl)
+    cols = np.array(sorted({0, 1, 63, 64, D // 2, D - 65, D - 2, D - 1}
+                           | set(np.random.default_rng(31).integers(0, D, 8).tolist())),
+                    dtype=np.int64)
+    oy, ohc, _ = oracle.mamba1_core(inp["x"], inp["w_conv"], inp["b_conv"], inp["delta"],
+                                    inp["A_log"], inp["B"], inp["C"], inp["D_vec"], inp["z"],
+                                    None, batch=B, seq_len=L, disc="zoh", cols=cols,
+                                    h_cache=True, h_last=True)
+    cc = torch.as_tensor(cols, device="cuda")
+    assert_close(host(y[:, cc].t()), oy, "y (sampled columns)")
+    assert_close(host(hc[0][:, cc].permute(1, 0, 2)), ohc, "h_cache (sampled columns)")
+    del hc
+
+
 @pytest.mark.parametrize("disc", DISCS)
 def test_decode_64_steps_sampled(disc):
     """256 sequences x 5120 channels, 64 consecutive single-token steps from a
