@@ -62,7 +62,7 @@ struct BwdCols {
     float* __restrict__ ddelta;
     float* __restrict__ dz;
     float* __restrict__ dh0;
-    float* __restrict__ ckpt;     // (waves, blocks per segment, 64, 8)
+    float* __restrict__ ckpt;     // (waves, blocks per segment, 2, 64, 4)
     float* __restrict__ partB;    // (B, tiles, L, 16)
     float* __restrict__ partC;    // (B, tiles, L, 16)
     float* __restrict__ partA;    // (waves, 64, 8)
@@ -145,7 +145,7 @@ struct Bwd {
     const uint32_t half;
     const bool gated;
     float4* lds;               // 8 steps: B rows [0, 32), C rows [32, 64) (16 floats per row)
-    float4* acache;            // aBar of a block's 8 steps: [step][lane][2] (8 floats per lane)
+    float4* acache;            // aBar of a block's 8 steps: [step][half][lane] (8 floats per lane)
 
     float A2[kH], Ai[kH], An[kH];
     float min_a2, dvec;
@@ -413,15 +413,16 @@ struct Bwd {
     }
 
     // ---- forward sweep over [ta, tb) in blocks of 8 from ta ---------------
-    // CKPT: store h at every block start to ck (2 KB per block, lane-major).
+    // CKPT: store h at every block start to ck (2 KB per block: states 0-3
+    // of the 64 lanes, then states 4-7, so each store is one contiguous 1 KB).
     template <bool CKPT>
     __device__ __forceinline__ void fwd_sweep(float (&h)[kH], int64_t ta, int64_t tb, float* ck) const {
         for (int64_t s = ta; s < tb; s += kT) {
             const int n = tb - s < kT ? static_cast<int>(tb - s) : kT;
             if constexpr (CKPT) {
-                float4* p = reinterpret_cast<float4*>(ck) + threadIdx.x * 2;
+                float4* p = reinterpret_cast<float4*>(ck) + threadIdx.x;
                 p[0] = make_float4(h[0], h[1], h[2], h[3]);
-                p[1] = make_float4(h[4], h[5], h[6], h[7]);
+                p[kWave] = make_float4(h[4], h[5], h[6], h[7]);
                 ck += kWave * kH;
             }
             float uu[kT], dv[kT];
@@ -529,8 +530,8 @@ struct Bwd {
             read_row(32, i, Cv);
             fwd<SM>(h, uu[i], dv[i], Bv, av);
             // aBar of the step, kept for the adjoint below (this lane only)
-            acache[(i * kWave + threadIdx.x) * 2] = make_float4(av[0], av[1], av[2], av[3]);
-            acache[(i * kWave + threadIdx.x) * 2 + 1] = make_float4(av[4], av[5], av[6], av[7]);
+            acache[(i * 2) * kWave + threadIdx.x] = make_float4(av[0], av[1], av[2], av[3]);
+            acache[(i * 2 + 1) * kWave + threadIdx.x] = make_float4(av[4], av[5], av[6], av[7]);
             if (i + 1 < kT) {
 #pragma unroll
                 for (int j = 0; j < kH; j++) hist[i + 1][j] = h[j];
@@ -555,8 +556,8 @@ struct Bwd {
             float Bv[kH], Cv[kH], dBp[kH];
             read_row(0, i, Bv);
             read_row(32, i, Cv);
-            const float4 a_lo = acache[(i * kWave + threadIdx.x) * 2];
-            const float4 a_hi = acache[(i * kWave + threadIdx.x) * 2 + 1];
+            const float4 a_lo = acache[(i * 2) * kWave + threadIdx.x];
+            const float4 a_hi = acache[(i * 2 + 1) * kWave + threadIdx.x];
             const float av[kH] = {a_lo.x, a_lo.y, a_lo.z, a_lo.w, a_hi.x, a_hi.y, a_hi.z, a_hi.w};
             float du_acc = 0.0f, ddv_acc = 0.0f;
             rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
@@ -630,8 +631,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             go[i] = bw.ld(c.dout, t);
             zz[i] = c.z ? bw.ld(c.z, t) : 0.0f;
         }
-        const float4* p = reinterpret_cast<const float4*>(ck + k * (kWave * kH)) + lane * 2;
-        const float4 h_lo = p[0], h_hi = p[1];
+        const float4* p = reinterpret_cast<const float4*>(ck + k * (kWave * kH)) + lane;
+        const float4 h_lo = p[0], h_hi = p[kWave];
         const float hin[kH] = {h_lo.x, h_lo.y, h_lo.z, h_lo.w, h_hi.x, h_hi.y, h_hi.z, h_hi.w};
         bw.stage(st);
 #pragma unroll
