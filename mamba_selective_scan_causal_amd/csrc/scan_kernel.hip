@@ -80,7 +80,9 @@ constexpr int kOutHC = 2;    // y and hCache
 
 // DN: every activation row stride is D and the B/C stride is N (dense
 // tensors); the strides then fold into one row offset per step.
-template <int DISC, int KS, int NS, bool DN>
+// HC: the hCache mode (a kernel of its own, so that the staging of the state
+// cache does not take registers from the kernel without it).
+template <int DISC, int KS, int NS, bool DN, bool HC>
 struct Scan {
     using L_t = Lane<KS, NS>;
     static constexpr int NR = L_t::NR;
@@ -92,21 +94,25 @@ struct Scan {
     const int64_t L, D;
     const int N, K;
     const uint32_t d;       // this lane's channel, clamped to D-1
+    const int64_t d0;       // the wave's first channel
     const int64_t b;
     const int64_t ldx, ldz, ldd, ldB, ldC, ldy;   // row strides (elements)
     const float* zsrc;      // z, or any valid array when ungated
     const bool gated;
     float4* lds;            // 64 float4 for this wave: B rows [0, 32), C rows [32, 64)
+    float4* hst;            // N = 16 hCache staging: lane l's states at [5 l, 5 l + 4)
 
     // Lanes past D compute channel D-1 again and store bit-identical values to
     // the same addresses as lane D-1, so no store needs a lane mask.
-    __device__ Scan(const Cols& c_, const ScanShape& s, int64_t b_, int64_t d_raw, float4* lds_)
+    __device__ Scan(const Cols& c_, const ScanShape& s, int64_t b_, int64_t d_raw, float4* lds_,
+                    float4* hst_)
         : c(c_), L(s.L), D(s.D), N(NS > 0 ? NS : s.N), K(KS > 0 ? KS : s.K),
-          d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)), b(b_),
+          d(static_cast<uint32_t>(d_raw < s.D ? d_raw : s.D - 1)),
+          d0(d_raw - static_cast<int64_t>(threadIdx.x)), b(b_),
           ldx(DN ? s.D : s.ld_src), ldz(DN ? s.D : (c_.z ? s.ld_z : s.ld_src)),
           ldd(DN ? s.D : s.ld_delta), ldB(DN ? N : s.ld_B), ldC(DN ? N : s.ld_C),
           ldy(DN ? s.D : s.ld_y),
-          zsrc(c_.z ? c_.z : c_.src), gated(c_.z != nullptr), lds(lds_) {}
+          zsrc(c_.z ? c_.z : c_.src), gated(c_.z != nullptr), lds(lds_), hst(hst_) {}
 
     __device__ __forceinline__ int64_t row(int64_t t) const { return b * L + t; }
     __device__ __forceinline__ float ld(const float* base, int64_t stride, int64_t t) const {
@@ -291,7 +297,25 @@ struct Scan {
             (c.y + r * ldy)[d] = gated ? yv * g : yv;
             if constexpr (OUT == kOutHC) {
                 float* __restrict__ hc = c.h_cache + r * D * N;
-                if constexpr (NS > 0 && NS % 4 == 0) {
+                if constexpr (NS == 16) {
+                    // The wave's 64 x 16 states of the step are one contiguous
+                    // 4 KB block: through LDS (80-byte lane stride, conflict
+                    // free) so that each 16-byte store instruction writes 1 KB
+                    // contiguously (a lane storing its own 64 bytes would
+                    // spread every store over 4 KB).  One wave per workgroup:
+                    // its LDS accesses complete in program order.
+                    const uint32_t lane = threadIdx.x;
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        hst[5 * lane + j] = make_float4(ln.h[4 * j], ln.h[4 * j + 1],
+                                                        ln.h[4 * j + 2], ln.h[4 * j + 3]);
+                    float4* hb = reinterpret_cast<float4*>(hc + d0 * 16);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int q = i * kWave + static_cast<int>(lane);
+                        if (d0 + q / 4 < D) hb[q] = hst[5 * (q / 4) + (q % 4)];
+                    }
+                } else if constexpr (NS > 0 && NS % 4 == 0) {
 #pragma unroll
                     for (int n = 0; n < NR; n += 4)
                         *reinterpret_cast<float4*>(hc + d * NS + n) =
@@ -383,7 +407,7 @@ struct Scan {
         }
         load_window(ln, tw);
         sweep<kWarm>(ln, tw, t0);
-        if (c.h_cache)
+        if constexpr (HC)
             sweep<kOutHC>(ln, t0, t1);
         else
             sweep<kOut>(ln, t0, t1);
@@ -397,10 +421,11 @@ struct Scan {
 
 // Two waves per SIMD: one wave alone issues VALU work only about every other
 // slot, so the register budget is capped at 256 VGPRs.
-template <int DISC, int KS, int NS, bool DN>
+template <int DISC, int KS, int NS, bool DN, bool HC>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_kernel(
     Cols c, ScanShape s) {
     __shared__ float4 lds[kWave];
+    __shared__ float4 hst[NS == 16 && HC ? 5 * kWave : 1];
     const int64_t lane = threadIdx.x;
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * s.seg;
     const int64_t g1 = g0 + s.seg < s.total ? g0 + s.seg : s.total;
@@ -412,7 +437,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
         const int64_t b = tile / s.tiles_per_b;
         const int64_t dt = tile - b * s.tiles_per_b;
-        Scan<DISC, KS, NS, DN> sc(c, s, b, dt * kWave + lane, lds);
+        Scan<DISC, KS, NS, DN, HC> sc(c, s, b, dt * kWave + lane, lds, hst);
         sc.run(t0, t1);
         g += t1 - t0;
     }
@@ -421,8 +446,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 template <int DISC, int KS, int NS, bool DN>
 hipError_t launch_t(const Cols& c, const ScanShape& s, hipStream_t st) {
     const int64_t nblk = (s.total + s.seg - 1) / s.seg;
-    hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN>), dim3(static_cast<unsigned>(nblk)),
-                       dim3(kWave), 0, st, c, s);
+    if (c.h_cache)
+        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, true>),
+                           dim3(static_cast<unsigned>(nblk)), dim3(kWave), 0, st, c, s);
+    else
+        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, false>),
+                           dim3(static_cast<unsigned>(nblk)), dim3(kWave), 0, st, c, s);
     return hipGetLastError();
 }
 
