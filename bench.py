@@ -157,6 +157,16 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
                                                 None, disc=disc, **kw),
                         stream, 10, before=lambda: flush.fill_(1.0))
     res["fused_cold_ms"] = _stats(cold)
+    # with the per-step state cache (a9): 64 more bytes written per (m, d)
+    hc = torch.empty((w.batch, w.seq_len, w.d_inner, w.d_state), device="cuda")
+    thc = _time_ms(lambda: mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"],
+                                           d["A_log"], d["B"], d["C"], d["D_vec"], d["z"], None,
+                                           disc=disc, h_cache=hc, **kw), stream, 5)
+    hc_bytes = algorithmic_bytes(w) + 4 * w.M * w.d_inner * w.d_state
+    res["fused_hcache"] = {"ms": thc, "algorithmic_bytes": hc_bytes,
+                           "GBps": hc_bytes / thc / 1e6,
+                           "frac_of_peak": hc_bytes / thc / 1e6 / HBM_PEAK_GBS}
+    del hc
     u = torch.empty_like(d["x"])
     tc = _time_ms(lambda: mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch,
                                           seq_len=w.seq_len, out=u, stream=stream), stream, 10)
