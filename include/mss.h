@@ -96,9 +96,11 @@ int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv,
  *   h0, h_last (B, D, N);  h_cache (B, L, D, N) = h_t after the update of step t.
  *   Optional (NULL allowed): D_vec (= 0), z (ungated output), h0 (= 0),
  *   h_cache, h_last.  Required: u, delta, A_log, B, C, y.
- *   The carried state between time segments processed in parallel drops
- *   contributions that have decayed by more than 2^-24 (see the design
- *   notes); the result is otherwise the plain recurrence in fp32.          */
+ *   Time is split into segments processed in parallel; a segment starting
+ *   at t0 > 0 rebuilds h(t0-1) by replaying the recurrence from h = 0 at the
+ *   step where every lane's slowest state has decayed by 2^-24 (or from
+ *   t = 0), so it drops contributions that have decayed by more than 2^-24;
+ *   the result is otherwise the plain recurrence in fp32.                  */
 int mss_selective_scan(const mss_dims* dims, int disc, const float* u, const float* delta,
                        const float* A_log, const float* B, const float* C, const float* D_vec,
                        const float* z, const float* h0, float* y, float* h_cache,
