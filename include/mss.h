@@ -169,8 +169,8 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
 
 /* ---- Backward passes ------------------------------------------------------
  * The reverse-time adjoint of the pages' CPU mirror (same diff and file,
- * function mamba1CpuBackward: the gate, "Selective scan, walked backwards in
- * time", the A_log clamp mask, softplus, SiLU and the depthwise conv1d).
+ * function mamba1CpuBackward: its gate, reverse-time selective-scan, A_log
+ * clamp mask, softplus, SiLU and depthwise conv1d parts).
  * Gradients are written, not accumulated.  Both entry points take a caller
  * workspace of at least mss_workspace_bytes bytes for the same dims and
  * device (256-byte aligned, overlapping nothing else; MSS_EWORKSPACE if

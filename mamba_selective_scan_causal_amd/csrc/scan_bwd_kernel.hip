@@ -2,8 +2,8 @@
 // gfx950.
 //
 // Computes the reverse-time adjoint of mamba1CpuBackward (builderforce-memory-
-// engine 2026.7.12 -> 2026.9.27, src/training/mamba1_cpu.ts: the gate, the
-// scan "walked backwards in time", the A_log clamp mask and softplus): per
+// engine 2026.7.12 -> 2026.9.27, src/training/mamba1_cpu.ts: its gate,
+// reverse-time scan, A_log clamp mask and softplus parts): per
 // (b, d) column, with dY = dout SiLU(z), g_n the adjoint carried from step
 // t+1 and dh_n = C_n dY + g_n,
 //   du = D dY + sum_n dh_n bBar_n            g_n <- dh_n aBar_n
