@@ -331,7 +331,7 @@ struct Scan {
 
     // Steps t0 .. t0+cnt-1 one at a time (not unrolled): loads its own
     // inputs and makes the fast/slow choice per step.  Used for the slow
-    // path, block remainders, the hCache mode and B/C without LDS staging.
+    // path, block remainders and B/C without LDS staging.
     // LDS: the block's B/C rows are staged (step i of the block at row i).
     template <int OUT, bool LDS>
     __device__ __forceinline__ void steps1(L_t& ln, int64_t t0, int cnt) const {
@@ -353,7 +353,7 @@ struct Scan {
     template <int OUT>
     __device__ __forceinline__ void sweep(L_t& ln, int64_t tb, int64_t te) const {
         if (tb >= te) return;
-        if constexpr (!kStage || OUT == kOutHC) {
+        if constexpr (!kStage) {
             for (int64_t t = tb; t < te; t += kT) {
                 const int cnt = te - t < kT ? static_cast<int>(te - t) : kT;
                 if constexpr (kStage) lds[threadIdx.x] = load_bc(t);
