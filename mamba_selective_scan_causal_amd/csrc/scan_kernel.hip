@@ -176,22 +176,33 @@ struct Scan {
         }
     }
 
-    // Inputs of steps t0 .. t0+kT-1 (rows past the sequence end are clamped
-    // to its last row; they are never used).
+    // Inputs of steps t0 .. t0+kT-1; rows past the sequence end (the
+    // prefetch after the last block starts at t0 = L) repeat its last row
+    // and are never used.  Wave-uniform row pointers advance by one row
+    // stride per step, so no step needs a row product.
     template <int OUT>
     __device__ __forceinline__ void load_block(float (&xs)[kT], float (&ds)[kT], float (&zs)[kT],
                                                int64_t t0) const {
+        const int64_t s0 = t0 < L ? t0 : L - 1;
+        const int64_t nv = L - s0;   // rows from s0 to the sequence end (>= 1)
+        const float* px = c.src + row(s0) * ldx;
+        const float* pd = c.delta + row(s0) * ldd;
+        const float* pz = zsrc + row(s0) * ldz;
 #pragma unroll
         for (int i = 0; i < kT; i++) {
-            const int64_t t = t0 + i < L ? t0 + i : L - 1;
-            xs[i] = ld(c.src, ldx, t);
-            ds[i] = ld(c.delta, ldd, t);
-            if constexpr (OUT != kWarm) zs[i] = ld(zsrc, ldz, t);
+            xs[i] = px[d];
+            ds[i] = pd[d];
+            if constexpr (OUT != kWarm) zs[i] = pz[d];
+            if (i + 1 < nv) {
+                px += ldx;
+                pd += ldd;
+                pz += ldz;
+            }
         }
     }
 
     // This lane's 16 bytes of the B rows (lanes 0-31) or C rows (lanes 32-63)
-    // of steps t0 .. t0+kT-1.
+    // of steps t0 .. t0+kT-1 (clamped to the last row like load_block).
     __device__ __forceinline__ float4 load_bc(int64_t t0) const {
         const uint32_t lane = threadIdx.x;
         const uint32_t q = lane & 31u;
