@@ -30,7 +30,9 @@
 // that step with h = 0 (state only, no outputs).  What this drops is exactly
 // the state at the replay start times a factor <= 2^-24 per state (the unit
 // roundoff of fp32: below one rounding of the state it came from); reaching
-// t = 0 makes it exact.  No workspace and no inter-wave synchronisation.
+// t = 0 makes it exact.  States that decay faster than the slowest one join
+// the replay later, each once its own decay to t0 reaches the same bound.
+// No workspace and no inter-wave synchronisation.
 #include "device_math.h"
 #include "launch.h"
 
@@ -144,9 +146,10 @@ struct Scan {
     }
 
     // First step of the forward replay: pick it by walking delta backwards.
-    __device__ __forceinline__ int64_t replay_start(const L_t& ln, int64_t t0) const {
+    // S returns the lane's sum of dv over [start, t0).
+    __device__ __forceinline__ int64_t replay_start(const L_t& ln, int64_t t0, float& S) const {
+        S = 0.0f;
         if (t0 == 0) return 0;
-        float S = 0.0f;
         int64_t t = t0;  // next step to visit is t - 1
         while (true) {
             float dd[kBackBlk];
@@ -212,13 +215,9 @@ struct Scan {
         return *reinterpret_cast<const float4*>(base + (q & 3u) * 4);
     }
 
-    // One time step.  SLOW: some lane has |dv A| < 2^-6 (see below).
-    // LDS: B_t / C_t come from the staged block at row i; otherwise from
-    // scalar loads.
-    template <int OUT, bool SLOW, bool LDS>
-    __device__ __forceinline__ void step(L_t& ln, float xv, float dv, float zv, int64_t t,
-                                         int i) const {
-        float u;
+    // The scan input of one step: conv1d + SiLU of x (fused; advances the
+    // conv window) or u itself.
+    __device__ __forceinline__ float scan_input(L_t& ln, float xv) const {
         if constexpr (kFused) {
             float acc = __builtin_fmaf(ln.w[0], xv, ln.bias);
 #pragma unroll
@@ -227,10 +226,26 @@ struct Scan {
 #pragma unroll
             for (int j = KR - 2; j > 0; j--) ln.xw[j] = ln.xw[j - 1];
             if constexpr (KR > 1) ln.xw[0] = xv;
-            u = silu(acc);
+            return silu(acc);
         } else {
-            u = xv;
+            return xv;
         }
+    }
+
+    // One time step.  SLOW: some lane has |dv A| < 2^-6 (see below).
+    // LDS: B_t / C_t come from the staged block at row i; otherwise from
+    // scalar loads.
+    template <int OUT, bool SLOW, bool LDS>
+    __device__ __forceinline__ void step(L_t& ln, float xv, float dv, float zv, int64_t t,
+                                         int i) const {
+        // The decays depend on dv alone: issued first, they overlap the
+        // input's conv and SiLU and the B/C reads.
+        float ab[NR];
+        if constexpr (!SLOW) {
+#pragma unroll
+            for (int n = 0; n < NR; n++) ab[n] = ex2(dv * ln.A2[n]);
+        }
+        const float u = scan_input(ln, xv);
         float Bv[NR], Cv[NR];
         if constexpr (LDS) {
 #pragma unroll
@@ -260,8 +275,7 @@ struct Scan {
 #pragma unroll
                 for (int n = 0; n < NR; n++) {
                     if (NS > 0 || n < N) {
-                        const float a = ex2(dv * ln.A2[n]);
-                        ln.h[n] = __builtin_fmaf(a, ln.h[n], dvu * Bv[n]);
+                        ln.h[n] = __builtin_fmaf(ab[n], ln.h[n], dvu * Bv[n]);
                         if constexpr (OUT != kWarm) yv = __builtin_fmaf(Cv[n], ln.h[n], yv);
                     }
                 }
@@ -270,9 +284,8 @@ struct Scan {
 #pragma unroll
                 for (int n = 0; n < NR; n++) {
                     if (NS > 0 || n < N) {
-                        const float a = ex2(dv * ln.A2[n]);
                         const float k = (u * ln.Ai[n]) * Bv[n];
-                        ln.h[n] = __builtin_fmaf(a, ln.h[n] + k, -k);
+                        ln.h[n] = __builtin_fmaf(ab[n], ln.h[n] + k, -k);
                         if constexpr (OUT != kWarm) yv = __builtin_fmaf(Cv[n], ln.h[n], yv);
                     }
                 }
@@ -406,18 +419,102 @@ struct Scan {
         }
     }
 
+    // Replay of steps [tb, te), state only; S = the lane's sum of dv over
+    // [tb, te).  The replay start was chosen for the slowest state; a faster
+    // state n joins only at the last block start from which its own decay
+    // to te, 2^(-|A2_n| sum dv), is still <= 2^-24 in every lane, and is 0
+    // until then.  That drops no more than the replay start itself drops, at
+    // a fraction of the cost when the decay rates differ (|A| = 1..16 makes
+    // the replay ~4x cheaper).  A replay from t = 0 is exact: every state
+    // runs from the start.
+    __device__ __forceinline__ void warm(L_t& ln, int64_t tb, int64_t te, float S) const {
+        if (tb >= te) return;
+        if constexpr (!kStage) {
+            sweep<kWarm>(ln, tb, te);
+        } else {
+            constexpr uint32_t kAll = (1u << NR) - 1u;
+            uint32_t act = tb == 0 ? kAll : 0u;   // wave-uniform set of running states
+            // S is kept by subtraction; slack bounds the rounding of the
+            // walk's sum and of the subtractions ((2 R + 16) u S over R
+            // steps), so S - slack is a lower bound of the exact remainder.
+            const float slack = S * (2.0f * static_cast<float>(te - tb) + 16.0f) * 0x1p-24f;
+            const float* ldsf = reinterpret_cast<const float*>(lds);
+            float nx[kT], nd[kT], nz[kT];
+            float4 nbc = load_bc(tb);
+            load_block<kWarm>(nx, nd, nz, tb);
+            int64_t t = tb;
+            for (; t + kT <= te; t += kT) {
+                float cx[kT], dv[kT];
+                float sdv = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kT; i++) {
+                    cx[i] = nx[i];
+                    dv[i] = softplus(nd[i]);
+                    sdv += dv[i];
+                }
+                lds[threadIdx.x] = nbc;
+                load_block<kWarm>(nx, nd, nz, t + kT);
+                nbc = load_bc(t + kT);
+                S -= sdv;   // remainder after this block
+                if (act != kAll) {
+#pragma unroll
+                    for (int n = 0; n < NR; n++)
+                        if (!(act & (1u << n)) &&
+                            wave_any((S - slack) * -ln.A2[n] < kDecayCut + 0.25f))
+                            act |= 1u << n;
+                }
+                if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {
+                    float w[kT];   // EULER: dv u; ZOH: u
+#pragma unroll
+                    for (int i = 0; i < kT; i++) {
+                        const float u = scan_input(ln, cx[i]);
+                        w[i] = DISC == MSS_DISC_EULER ? dv[i] * u : u;
+                    }
+                    // State-major: each running state takes the block's 8
+                    // steps in a row (B_t[n] of step i is float i*16 + n).
+#pragma unroll
+                    for (int n = 0; n < NR; n++) {
+                        if (act & (1u << n)) {
+#pragma unroll
+                            for (int i = 0; i < kT; i++) {
+                                const float Bv = ldsf[i * 16 + n];
+                                const float a = ex2(dv[i] * ln.A2[n]);
+                                if constexpr (DISC == MSS_DISC_EULER) {
+                                    ln.h[n] = __builtin_fmaf(a, ln.h[n], w[i] * Bv);
+                                } else {
+                                    const float k = (w[i] * ln.Ai[n]) * Bv;
+                                    ln.h[n] = __builtin_fmaf(a, ln.h[n] + k, -k);
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    // the accurate path for every state (a state that had not
+                    // joined starts early, from 0: only more exact)
+                    steps1<kWarm, true>(ln, t, kT);
+                    act = kAll;
+                }
+            }
+            if (t < te) {
+                lds[threadIdx.x] = nbc;
+                steps1<kWarm, true>(ln, t, static_cast<int>(te - t));
+            }
+        }
+    }
+
     // Produce outputs for steps [t0, t1) of this column.
     __device__ __forceinline__ void run(int64_t t0, int64_t t1) const {
         L_t ln;
         init(ln);
-        const int64_t tw = replay_start(ln, t0);
+        float S;
+        const int64_t tw = replay_start(ln, t0, S);
         if (tw == 0 && c.h0) {
 #pragma unroll
             for (int n = 0; n < NR; n++)
                 if (NS > 0 || n < N) ln.h[n] = c.h0[(b * D + d) * N + n];
         }
         load_window(ln, tw);
-        sweep<kWarm>(ln, tw, t0);
+        warm(ln, tw, t0, S);
         if constexpr (HC)
             sweep<kOutHC>(ln, t0, t1);
         else
