@@ -7,6 +7,9 @@ y = sum_n C h + D u, SiLU(z) gate -- the fused mss_mamba1_core kernel -- on the
 block, inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--disc zoh|euler] [--no-cpu-baseline]
+
+The default 20 warm-up calls (~20 ms) let the clock settle: under this
+VALU-heavy load it drops after the first few calls and recovers over ~20.
 """
 from __future__ import annotations
 
@@ -391,7 +394,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--disc", default="zoh", choices=("zoh", "euler"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",

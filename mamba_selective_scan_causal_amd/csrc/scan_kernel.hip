@@ -457,10 +457,13 @@ struct Scan {
                 nbc = load_bc(t + kT);
                 S -= sdv;   // remainder after this block
                 if (act != kAll) {
+                    // Written as "not provably decayed enough", so that a
+                    // non-finite sum (an infinite delta makes S - slack NaN)
+                    // lets the state join.
 #pragma unroll
                     for (int n = 0; n < NR; n++)
                         if (!(act & (1u << n)) &&
-                            wave_any((S - slack) * -ln.A2[n] < kDecayCut + 0.25f))
+                            wave_any(!((S - slack) * -ln.A2[n] >= kDecayCut + 0.25f)))
                             act |= 1u << n;
                 }
                 if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {

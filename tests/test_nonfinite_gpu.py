@@ -65,6 +65,38 @@ def test_core_contains_nonfinite_inputs(disc):
 
 
 @pytest.mark.parametrize("disc", DISCS)
+def test_core_infinite_delta_inside_a_replay_window(disc):
+    """+Inf in delta a few steps before a segment start, so dv = +Inf lies
+    inside the window the segment replays (its backward walk stops there) and
+    the replay's remaining sum of dv is infinite; every state must still take
+    part in the replay.  This shape is cut into segments of 512 steps of the
+    flattened (column tile, t) space: row 1's tiles start segments at
+    t = 72, 584, 1096 (channels 0-63) and t = 108, 620, 1132 (64-99).  ZOH:
+    aBar = 0 resets the column there and every output stays finite; EULER:
+    dv B u is infinite, the column is non-finite from there on.  Outputs are
+    compared wherever the oracle is finite."""
+    import torch
+    w = W
+    inp = gen.generate(w)
+    L = w.seq_len
+    for t, ch in ((612, 70), (1125, 99), (580, 5)):
+        inp["delta"][1 * L + t, ch] = np.inf
+    d = {k: dev(v) for k, v in inp.items()}
+    B, D, N = w.batch, w.d_inner, w.d_state
+    y, hl = nan_like((B * L, D)), nan_like((B, D, N))
+    mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                    d["D_vec"], d["z"], d["h0"], batch=B, seq_len=L, disc=disc, h_last=hl, out=y)
+    torch.cuda.synchronize()
+    oy, _, ohl = oracle.mamba1_core(inp["x"], inp["w_conv"], inp["b_conv"], inp["delta"],
+                                    inp["A_log"], inp["B"], inp["C"], inp["D_vec"], inp["z"],
+                                    inp["h0"], batch=B, seq_len=L, disc=disc, h_last=True)
+    if disc == "zoh":
+        assert np.isfinite(oy).all()
+    assert_close(host(y), oy, "y")
+    assert_close(host(hl), ohl, "h_last")
+
+
+@pytest.mark.parametrize("disc", DISCS)
 def test_decode_step_contains_nonfinite_inputs(disc):
     import torch
     w = gen.DECODE.with_(name="nonfinite_decode", batch=8, d_inner=256, seq_len=3)
