@@ -9,16 +9,20 @@
 
 namespace mss {
 
-// Backward of the scan: one wave per (batch row, 32-channel tile, segment of
-// `seg` steps, a multiple of 8).  Workspace regions (all fp32):
+// Backward of the scan: the flattened (tile, t) space of the B * tiles_per_b
+// channel tiles (batch row, 32 channels) is cut into `waves` segments of
+// `seg` steps, one wave each; a segment crossing the end of a tile is worked
+// as one piece per tile, and a tile has at most `pieces` pieces.  Workspace
+// regions (all fp32):
 //   ckpt  (waves, blocks_per_seg, 64, 8)   h at every 8-step block start
 //   partB, partC (B, tiles_per_b, L, 16)    per-tile dB / dC rows
-//   partA (waves, 64, 8), partD (waves, 32) per-wave dA / dD sums
+//   partA (tiles, pieces, 64, 8), partD (tiles, pieces, 32)  per-piece dA / dD sums
 struct BwdShape {
     int64_t B, L, D;
     int N;
     int64_t tiles_per_b;      // ceil(D / 32)
-    int64_t nseg, seg, blocks_per_seg;
+    int64_t total;            // B * tiles_per_b * L
+    int64_t seg, waves, blocks_per_seg, pieces;
     bool bc_vec;              // B and C rows 16-byte aligned (N = 16)
 };
 

@@ -249,10 +249,10 @@ constexpr int64_t kConvPartRows = 9; // kMaxK + 1
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Work split of the scan backward: enough segments per (batch row, channel
-// tile) to give about two waves per SIMD, but no segment shorter than
-// MSS_BWD_MIN_SEG steps (default 256), so that the two decay replays of a
-// segment stay a small fraction of its work.
+// Work split of the scan backward: the flattened (channel tile, t) space cut
+// into segments of equal length, about two waves per SIMD, but no segment
+// shorter than MSS_BWD_MIN_SEG steps (default 256), so that the two decay
+// replays of a segment stay a small fraction of its work.
 mss::BwdShape bwd_shape(const mss_dims* dims) {
     static const int64_t waves_per_cu = env_or("MSS_BWD_WAVES_PER_CU", 8);
     static const int64_t min_seg = env_or("MSS_BWD_MIN_SEG", 256);
@@ -262,17 +262,16 @@ mss::BwdShape bwd_shape(const mss_dims* dims) {
     s.D = dims->d_inner;
     s.N = static_cast<int>(dims->d_state);
     s.tiles_per_b = (s.D + kBwdTile - 1) / kBwdTile;
-    const int64_t tiles = s.B * s.tiles_per_b;
+    s.total = s.B * s.tiles_per_b * s.L;   // fits: B L D was counted without overflow
     const int64_t target = cu_count() * waves_per_cu;
-    int64_t nseg = tiles > 0 ? target / tiles : 1;
-    const int64_t max_seg = (s.L + min_seg - 1) / min_seg;
-    if (nseg > max_seg) nseg = max_seg;
-    if (nseg < 1) nseg = 1;
-    s.seg = align_up((s.L + nseg - 1) / (nseg > 0 ? nseg : 1), kBwdBlock);
-    if (s.seg < kBwdBlock) s.seg = kBwdBlock;
-    s.nseg = (s.L + s.seg - 1) / s.seg;
-    if (s.nseg < 1) s.nseg = 1;
-    s.blocks_per_seg = s.seg / kBwdBlock;
+    int64_t seg = (s.total + target - 1) / target;
+    if (seg < min_seg) seg = min_seg;
+    if (seg < 1) seg = 1;
+    s.seg = seg;
+    s.waves = (s.total + seg - 1) / seg;
+    s.blocks_per_seg = (seg + kBwdBlock - 1) / kBwdBlock;
+    // a tile of L steps meets at most ceil(L / seg) + 1 segments
+    s.pieces = (s.L + seg - 1) / seg + 1;
     s.bc_vec = false;
     return s;
 }
@@ -283,11 +282,11 @@ struct BwdLayout {
 };
 
 bool bwd_layout(const mss::BwdShape& s, BwdLayout& o) {
-    const int64_t waves = s.B * s.tiles_per_b * s.nseg;
     int64_t ck, pb, pa, pd;
-    if (!count(ck, {waves, s.blocks_per_seg, 64 * 8 * 4}) ||
-        !count(pb, {s.B, s.tiles_per_b, s.L, 16 * 4}) || !count(pa, {waves, 64 * 8 * 4}) ||
-        !count(pd, {waves, 32 * 4}))
+    if (!count(ck, {s.waves, s.blocks_per_seg, 64 * 8 * 4}) ||
+        !count(pb, {s.B, s.tiles_per_b, s.L, 16 * 4}) ||
+        !count(pa, {s.B, s.tiles_per_b, s.pieces, 64 * 8 * 4}) ||
+        !count(pd, {s.B, s.tiles_per_b, s.pieces, 32 * 4}))
         return false;
     o.ckpt = 0;
     o.partB = align_up(o.ckpt + ck, 256);
@@ -396,7 +395,7 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
     if (MD > 0) {
         s = bwd_shape(dims);
         if (!bwd_layout(s, lay)) return MSS_EINVAL;
-        if (s.B * s.tiles_per_b * s.nseg > INT32_MAX) return MSS_EINVAL;   // grid size
+        if (s.waves > INT32_MAX) return MSS_EINVAL;   // grid size
         need = lay.total;
     }
     // The workspace is an output like the others: it may not overlap anything.

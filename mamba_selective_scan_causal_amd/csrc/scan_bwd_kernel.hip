@@ -12,12 +12,15 @@
 //   dB[r,n] = sum_d dh_n u dbBar_n/dB          dC[r,n] = sum_d dY h_t,n
 //   dz = dout y SiLU'(z),  ddelta = ddv sigmoid(delta),  dD = sum dY u
 //
-// Mapping.  One wave64 per (batch row, 32 channels, time segment); lane
-// (half, q) owns channel q of the tile and the 8 states n = 8 half + j, so
-// the per-lane state vectors (h, adjoint, dA) stay at 8 registers each and
-// the two halves of a channel combine their sums with one cross-half add.
+// Mapping.  A channel tile is (batch row, 32 channels); lane (half, q) owns
+// channel q of the tile and the 8 states n = 8 half + j, so the per-lane
+// state vectors (h, adjoint, dA) stay at 8 registers each and the two halves
+// of a channel combine their sums with one cross-half add.  The flattened
+// (tile, t) space is cut into equal segments, one wave each, so that all
+// wave slots carry the same work; a segment that crosses the end of a tile
+// is worked as one piece per tile.
 //
-// Work per segment [t0, t1):
+// Work per piece [t0, t1) of a tile:
 //   1. h(t0-1) by decay-bounded forward replay (as in the forward kernel).
 //   2. Forward over the segment, storing h at every 8-step block start in the
 //      checkpoint workspace (2 KB per block).
@@ -32,7 +35,7 @@
 // over the 32 channels of the tile with a transpose-reduce (one exchange
 // level per lane bit, DPP and ds_swizzle), then written per tile to a
 // partial buffer that a second kernel sums over tiles in a fixed order; dA
-// and dD are written per wave and summed the same way.  No atomics: the
+// and dD are written per piece and summed the same way.  No atomics: the
 // result is bitwise reproducible.
 #include "device_math.h"
 #include "launch_bwd.h"
@@ -575,18 +578,16 @@ struct Bwd {
     }
 };
 
+// One piece [t0, t1) of channel tile ti (batch row b = ti / tiles_per_b);
+// slot: the piece's index among the pieces of tile ti, which selects its
+// rows of partA and partD; ck: this wave's checkpoint area.
 template <int DISC, int NS>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_bwd_kernel(
-    BwdCols c, BwdShape s) {
-    __shared__ float4 lds[kWave + kT * kWave * 2];   // B/C staging, then the aBar cache
-    const int64_t w = blockIdx.x;
-    const int64_t ti = w / s.nseg;
-    const int64_t sg = w - ti * s.nseg;
+__device__ __forceinline__ void bwd_piece(const BwdCols& c, const BwdShape& s, int64_t ti,
+                                          int64_t t0, int64_t t1, int64_t slot, float* ck,
+                                          float4* lds) {
     const int64_t b = ti / s.tiles_per_b;
     const int64_t ct = ti - b * s.tiles_per_b;
     const uint32_t lane = threadIdx.x;
-    const int64_t t0 = sg * s.seg;
-    const int64_t t1 = t0 + s.seg < s.L ? t0 + s.seg : s.L;
 
     Bwd<DISC, NS> bw(c, s, b, ct * 32 + (lane & 31u), lds);
     bw.init();
@@ -599,8 +600,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         h[j] = (tw == 0 && c.h0 && bw.valid(j)) ? c.h0[(b * s.D + bw.d) * bw.N + bw.half * kH + j] : 0.0f;
     bw.template fwd_sweep<false>(h, tw, t0, nullptr);
 
-    // 2. checkpoints of the segment
-    float* ck = c.ckpt + w * s.blocks_per_seg * (kWave * kH);
+    // 2. checkpoints of the piece
     bw.template fwd_sweep<true>(h, t0, t1, ck);
     // The checkpoints are read back by this wave below.
     __threadfence_block();
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int j = 0; j < kH; j++) g[j] = 0.0f;
     bw.rev_sweep(g, t1, bw.replay_end(t1));
 
-    // 4. blocks of the segment, newest first
+    // 4. blocks of the piece, newest first
     float dA[kH];
 #pragma unroll
     for (int j = 0; j < kH; j++) dA[j] = 0.0f;
@@ -646,11 +646,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             bw.template block<kAll>(g, dA, dD, hin, st, n, uu, dl, dv, go, zz, pB, pC);
     }
 
-    // 5. per-wave partial sums and dh0
-    float4* pa = reinterpret_cast<float4*>(c.partA + (w * kWave + lane) * kH);
+    // 5. the piece's partial sums and dh0
+    const int64_t row = ti * s.pieces + slot;
+    float4* pa = reinterpret_cast<float4*>(c.partA + (row * kWave + lane) * kH);
     pa[0] = make_float4(dA[0], dA[1], dA[2], dA[3]);
     pa[1] = make_float4(dA[4], dA[5], dA[6], dA[7]);
-    if (lane < 32) c.partD[w * 32 + lane] = dD;
+    if (lane < 32) c.partD[row * 32 + lane] = dD;
     if (t0 == 0 && c.dh0 && bw.live) {
 #pragma unroll
         for (int j = 0; j < kH; j++)
@@ -658,10 +659,36 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
 }
 
-// Cross-tile and cross-segment sums, fixed order:
+// Wave w takes steps [w seg, (w+1) seg) of the flattened (tile, t) space,
+// so every wave has the same number of steps; a range that crosses the end
+// of a tile is taken as one piece per tile, one after the other.
+template <int DISC, int NS>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_bwd_kernel(
+    BwdCols c, BwdShape s) {
+    __shared__ float4 lds[kWave + kT * kWave * 2];   // B/C staging, then the aBar cache
+    const int64_t w = blockIdx.x;
+    const int64_t g0 = w * s.seg;
+    const int64_t g1 = g0 + s.seg < s.total ? g0 + s.seg : s.total;
+    float* ck = c.ckpt + w * s.blocks_per_seg * (kWave * kH);
+    for (int64_t g = g0; g < g1;) {
+        const int64_t ti = g / s.L;
+        const int64_t t0 = g - ti * s.L;
+        const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
+        const int64_t slot = w - (ti * s.L) / s.seg;   // waves before w that cover tile ti
+        bwd_piece<DISC, NS>(c, s, ti, t0, t1, slot, ck, lds);
+        g += t1 - t0;
+    }
+}
+
+// Number of pieces of tile ti (one per wave whose step range meets it).
+__device__ __forceinline__ int64_t tile_pieces(const BwdShape& s, int64_t ti) {
+    return (ti * s.L + s.L - 1) / s.seg - (ti * s.L) / s.seg + 1;
+}
+
+// Cross-tile and cross-piece sums, fixed order:
 //   dB[r, n], dC[r, n] = sum over channel tiles of the partial rows;
-//   dA_log[d, n] = A[d, n] * sum over (b, segment) (0 outside the clamp);
-//   dD[d] = sum over (b, segment).
+//   dA_log[d, n] = A[d, n] * sum over (b, piece) (0 outside the clamp);
+//   dD[d] = sum over (b, piece).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdCols c, BwdShape s, float* dB,
                                                          float* dC, float* dA_log, float* dD) {
     const int64_t M = s.B * s.L;
@@ -687,20 +714,23 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdCols c, BwdShape s, 
             const int64_t ct = d / 32, q = d - ct * 32;
             const int64_t lane = (n / kH) * 32 + q, j = n % kH;
             float acc = 0.0f;
-            for (int64_t b = 0; b < s.B; b++)
-                for (int64_t sg = 0; sg < s.nseg; sg++) {
-                    const int64_t w = (b * s.tiles_per_b + ct) * s.nseg + sg;
-                    acc += c.partA[(w * kWave + lane) * kH + j];
-                }
+            for (int64_t b = 0; b < s.B; b++) {
+                const int64_t ti = b * s.tiles_per_b + ct;
+                const int64_t np = tile_pieces(s, ti);
+                for (int64_t p = 0; p < np; p++)
+                    acc += c.partA[((ti * s.pieces + p) * kWave + lane) * kH + j];
+            }
             const float al = c.A_log[e];
             dA_log[e] = (al <= -10.0f || al >= 5.0f) ? 0.0f : acc * a_cont(al);
         } else {
             const int64_t d = i - nBC - nA;
             const int64_t ct = d / 32, q = d - ct * 32;
             float acc = 0.0f;
-            for (int64_t b = 0; b < s.B; b++)
-                for (int64_t sg = 0; sg < s.nseg; sg++)
-                    acc += c.partD[((b * s.tiles_per_b + ct) * s.nseg + sg) * 32 + q];
+            for (int64_t b = 0; b < s.B; b++) {
+                const int64_t ti = b * s.tiles_per_b + ct;
+                const int64_t np = tile_pieces(s, ti);
+                for (int64_t p = 0; p < np; p++) acc += c.partD[(ti * s.pieces + p) * 32 + q];
+            }
             dD[d] = acc;
         }
     }
@@ -708,9 +738,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdCols c, BwdShape s, 
 
 template <int DISC, int NS>
 hipError_t launch_t(const BwdCols& c, const BwdShape& s, hipStream_t st) {
-    const int64_t nw = s.B * s.tiles_per_b * s.nseg;
-    hipLaunchKernelGGL((scan_bwd_kernel<DISC, NS>), dim3(static_cast<unsigned>(nw)), dim3(kWave),
-                       0, st, c, s);
+    hipLaunchKernelGGL((scan_bwd_kernel<DISC, NS>), dim3(static_cast<unsigned>(s.waves)),
+                       dim3(kWave), 0, st, c, s);
     return hipGetLastError();
 }
 
