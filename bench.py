@@ -131,9 +131,10 @@ def _stats(ts):
 
 
 def extras(w, inp, d, y, disc, stream, with_oracle=True):
-    """Side measurements: the other discretisation, the unfused path (conv
-    kernel, then the scan on u), and the decode workload (256 sequences x
-    5120 channels, 64 consecutive single-token steps)."""
+    """Side measurements: the other discretisation, the fused core reading
+    column slices of the projection outputs, the unfused path (conv kernel,
+    then the scan on u), and the decode workload (256 sequences x 5120
+    channels, 64 consecutive single-token steps)."""
     import torch
     import mamba_selective_scan_causal_amd as mss
     from mamba_selective_scan_causal_amd import inputs as gen
@@ -170,6 +171,36 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
                            "GBps": hc_bytes / thc / 1e6,
                            "frac_of_peak": hc_bytes / thc / 1e6 / HBM_PEAK_GBS}
     del hc
+    # the layout inside a Mamba-1 block: x and z the two halves of the
+    # (M, 2D) in_proj output, B and C columns of the (M, R + 2N) x_proj
+    # output (R = D / 16, the dt rank), read in place through row strides
+    Dm, Nm = w.d_inner, w.d_state
+    R = Dm // 16
+    XZ = torch.empty((w.M, 2 * Dm), device="cuda")
+    XZ[:, :Dm].copy_(d["x"])
+    XZ[:, Dm:].copy_(d["z"])
+    XP = torch.zeros((w.M, R + 2 * Nm), device="cuda")
+    XP[:, R:R + Nm].copy_(d["B"])
+    XP[:, R + Nm:].copy_(d["C"])
+
+    def strided(m):
+        return lambda: mss.mamba1_core(XZ[:, :Dm], d["w_conv"], d["b_conv"], d["delta"],
+                                       d["A_log"], XP[:, R:R + Nm], XP[:, R + Nm:], d["D_vec"],
+                                       XZ[:, Dm:], None, disc=m, **kw)
+
+    def dense(m):
+        return lambda: mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"],
+                                       d["B"], d["C"], d["D_vec"], d["z"], None, disc=m, **kw)
+    # alternating rounds, so that both layouts see the same clock
+    ts = {k: [] for k in ("s", "d")}
+    for _ in range(4):
+        ts["s"] += _event_times(strided(disc), stream, 5)
+        ts["d"] += _event_times(dense(disc), stream, 5)
+    res["fused_strided"] = {"layout": f"x, z halves of ({w.M}, {2 * Dm}); B, C columns of "
+                                      f"({w.M}, {R + 2 * Nm}); delta, y dense",
+                            "disc": disc,
+                            "strided_ms": _stats(ts["s"]), "dense_ms": _stats(ts["d"])}
+    del XZ, XP
     u = torch.empty_like(d["x"])
     tc = _time_ms(lambda: mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch,
                                           seq_len=w.seq_len, out=u, stream=stream), stream, 10)
