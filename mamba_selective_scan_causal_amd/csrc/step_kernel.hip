@@ -8,8 +8,10 @@
 // HBM-bound: per (b, d) it reads and writes h (2 * 4N bytes) and the conv
 // window (2 * 4(K-1) bytes) plus x, z, delta, y.
 //
-// N = 16 (step16_kernel): a wave takes 64 channels of two batch rows, and
-// h, like A_log, is moved in 16-byte pieces with consecutive lanes on
+// N = 16 (step16_kernel): a wave keeps one tile of 64 channels -- their A,
+// 1/A and conv taps are computed once -- and takes batch rows two at a time
+// from a set of groups shared evenly between the waves of that tile.  h,
+// like A_log, is moved in 16-byte pieces with consecutive lanes on
 // consecutive pieces, so every h access is one contiguous 1 KB.  Lane
 // (m, s) = (lane / 4, lane % 4) holds piece i = 0..3 of the block: states
 // 4 s .. 4 s + 3 of channel 16 i + m, and updates those 16 (channel, state)
@@ -26,9 +28,8 @@ namespace {
 
 constexpr float kSmallX = 0.015625f;          // same ZOH expm1 switch as the scan
 
-// Batch rows per wave: the per-channel parameters (A, 1/A, conv taps) are
-// loaded and transformed once for kRows rows, and all loads of the rows are
-// issued before any arithmetic so that their latencies overlap.
+// Batch rows per group: all loads of a group's rows are issued before any
+// arithmetic so that their latencies overlap.
 constexpr int kRows = 2;
 
 // The value of lane ^ B (B = 1 or 2) inside its quad (DPP quad_perm).
@@ -92,13 +93,40 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
     const uint32_t lane = threadIdx.x, m = lane >> 2, s = lane & 3u;
     const int64_t tiles = (a.D + kWave - 1) / kWave;
     const int64_t groups = (a.B + kRows - 1) / kRows;
-    const int64_t nblk = groups * tiles;
-    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t g = blk / tiles;
-        const int64_t d0 = (blk - g * tiles) * kWave;   // first channel of the tile
-        const int64_t d_own = d0 + 16 * s + m;         // the channel this lane owns
-        const bool valid = d_own < a.D;
-        const int64_t d = valid ? d_own : a.D - 1;
+    // wave w keeps channel tile w % tiles and takes the batch groups
+    // w / tiles, + G, + 2 G, ... (the grid is tiles * G waves)
+    const int64_t G = gridDim.x / tiles;
+    const int64_t d0 = (blockIdx.x % tiles) * kWave;   // first channel of the tile
+    const int64_t d_own = d0 + 16 * s + m;             // the channel this lane owns
+    const bool valid = d_own < a.D;
+    const int64_t d = valid ? d_own : a.D - 1;
+    // piece i of this lane: channel d0 + 16 i + m, states 4 s .. 4 s + 3
+    bool pvalid[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) pvalid[i] = d0 + 16 * i + m < a.D;
+    // A of the lane's 16 (channel, state) pairs, laid out like h
+    float A2[4][4], Ai[4][4];
+    {
+        const float4* src = reinterpret_cast<const float4*>(a.A_log + d0 * 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (pvalid[i]) t = src[i * kWave + lane];
+            const float al[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float A = pvalid[i] ? a_cont_fast(al[k]) : -1.0f;
+                A2[i][k] = A * kLog2e;
+                Ai[i][k] = rcp(A);
+            }
+        }
+    }
+    float w[KR];
+#pragma unroll
+    for (int k = 0; k < KR; k++) w[k] = k < K ? a.w_conv[d * K + k] : 0.0f;
+    const float bias = a.b_conv ? a.b_conv[d] : 0.0f;
+    const float dvec = a.D_vec ? a.D_vec[d] : 0.0f;
+    for (int64_t g = blockIdx.x / tiles; g < groups; g += G) {
         int64_t bs[kRows];
         bool live[kRows];
 #pragma unroll
@@ -107,10 +135,6 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
             live[r] = b < a.B;            // wave-uniform
             bs[r] = live[r] ? b : a.B - 1;
         }
-        // piece i of this lane: channel d0 + 16 i + m, states 4 s .. 4 s + 3
-        bool pvalid[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) pvalid[i] = d0 + 16 * i + m < a.D;
 
         // --- every load first.  B and C rows of the kRows batch entries are
         // one float per lane, staged through LDS.
@@ -138,28 +162,6 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
                 h[r][i][0] = t.x; h[r][i][1] = t.y; h[r][i][2] = t.z; h[r][i][3] = t.w;
             }
         }
-        // A of the lane's 16 (channel, state) pairs, laid out like h
-        float A2[4][4], Ai[4][4];
-        {
-            const float4* src = reinterpret_cast<const float4*>(a.A_log + d0 * 16);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (pvalid[i]) t = src[i * kWave + lane];
-                const float al[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const float A = pvalid[i] ? a_cont_fast(al[k]) : -1.0f;
-                    A2[i][k] = A * kLog2e;
-                    Ai[i][k] = rcp(A);
-                }
-            }
-        }
-        float w[KR];
-#pragma unroll
-        for (int k = 0; k < KR; k++) w[k] = k < K ? a.w_conv[d * K + k] : 0.0f;
-        const float bias = a.b_conv ? a.b_conv[d] : 0.0f;
-        const float dvec = a.D_vec ? a.D_vec[d] : 0.0f;
         __syncthreads();
         float Bv[kRows][4], Cv[kRows][4];
 #pragma unroll
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
                             k == 1 ? xv[r] : prev[r][k >= 2 ? k - 2 : 0];
             }
         }
-        __syncthreads();   // the next tile's B/C rows reuse bcs
+        __syncthreads();   // the next group's B/C rows reuse bcs
     }
 }
 
@@ -313,10 +315,22 @@ __global__ __launch_bounds__(kWave) void step_kernel(StepArgs a) {
 
 template <int DISC, int KS>
 hipError_t launch_n(const StepArgs& a, unsigned grid, hipStream_t st) {
-    if (a.N == 16)
-        hipLaunchKernelGGL((step16_kernel<DISC, KS>), dim3(grid), dim3(kWave), 0, st, a);
-    else
+    if (a.N == 16) {
+        // tiles x G waves, G batch-group slots per tile: about 3072 waves (three
+        // per SIMD), each taking the same number of groups
+        const int64_t tiles = (a.D + kWave - 1) / kWave;
+        const int64_t groups = (a.B + kRows - 1) / kRows;
+        int64_t G = (3072 + tiles - 1) / tiles;
+        if (G > groups) G = groups;
+        if (G < 1) G = 1;
+        const int64_t per = (groups + G - 1) / G;
+        G = (groups + per - 1) / per;
+        if (tiles * G > INT32_MAX) return hipErrorInvalidValue;   // grid size
+        hipLaunchKernelGGL((step16_kernel<DISC, KS>), dim3(static_cast<unsigned>(tiles * G)),
+                           dim3(kWave), 0, st, a);
+    } else {
         hipLaunchKernelGGL((step_kernel<DISC, KS>), dim3(grid), dim3(kWave), 0, st, a);
+    }
     return hipGetLastError();
 }
 
