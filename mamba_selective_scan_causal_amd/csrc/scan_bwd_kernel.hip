@@ -122,11 +122,8 @@ __device__ __forceinline__ float reduce8(const float (&v)[kH]) {
     return w1;
 }
 
-// d SiLU / dv = s (1 + v (1 - s)), s = sigmoid(v).
-__device__ __forceinline__ float silu_grad(float v) {
-    const float s = rcp(1.0f + ex2(-kLog2e * v));
-    return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
-}
+// sigmoid(v); SiLU(v) = v sigmoid(v) and d SiLU / dv = s (1 + v (1 - s)) with
+// s = sigmoid(v) are formed from it where used.
 __device__ __forceinline__ float sigmoid(float v) { return rcp(1.0f + ex2(-kLog2e * v)); }
 
 // expm1(x) for |x| < 2^-6 (relative truncation < 2e-7) else a - 1.
@@ -254,15 +251,24 @@ struct Bwd {
     template <int SM>
     __device__ __forceinline__ void fwd(float (&h)[kH], float uv, float dv, const float (&Bv)[kH],
                                         float (&av)[kH]) const {
+        fwd<SM>(h, h, uv, dv, Bv, av);
+    }
+    // The same from hin into hout (hin is left as it was).
+    template <int SM>
+    __device__ __forceinline__ void fwd(const float (&hin)[kH], float (&hout)[kH], float uv,
+                                        float dv, const float (&Bv)[kH], float (&av)[kH]) const {
         const float dvu = dv * uv;
 #pragma unroll
         for (int j = 0; j < kH; j++) {
             av[j] = 0.0f;
-            if (!valid(j)) continue;
-            if (slow_state<SM>(j))
-                fwd_state<true>(j, h[j], uv, dv, dvu, Bv[j], av[j]);
-            else
-                fwd_state<false>(j, h[j], uv, dv, dvu, Bv[j], av[j]);
+            float hv = hin[j];
+            if (valid(j)) {
+                if (slow_state<SM>(j))
+                    fwd_state<true>(j, hv, uv, dv, dvu, Bv[j], av[j]);
+                else
+                    fwd_state<false>(j, hv, uv, dv, dvu, Bv[j], av[j]);
+            }
+            hout[j] = hv;
         }
     }
 
@@ -281,10 +287,10 @@ struct Bwd {
     // FULL steps take aBar from the block's recompute (a_in); the replay
     // computes it.
     template <bool SLOW, bool FULL>
-    __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float uv,
-                                              float dv, float udv, float dY, float Bj, float Cj,
-                                              float a_in, float& du_acc, float& ddv_acc,
-                                              float& dBp) const {
+    __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float ht,
+                                              float uv, float dv, float udv, float dY, float Bj,
+                                              float Cj, float a_in, float& du_acc,
+                                              float& ddv_acc, float& dBp) const {
         const float x2 = (SLOW || !FULL) ? dv * A2[j] : 0.0f;
         const float a = FULL ? a_in : ex2(x2);
         const float dh = __builtin_fmaf(Cj, dY, g);
@@ -311,7 +317,9 @@ struct Bwd {
                 ddv_acc = __builtin_fmaf(gn, __builtin_fmaf(hp, An[j], uB), ddv_acc);
                 float inner;
                 if constexpr (!SLOW) {
-                    inner = __builtin_fmaf(dv, a * (hp + K), -(K * q));
+                    // aBar (h_{t-1} + K) = h_t + K on the fast path, whose
+                    // update is h_t = aBar (h_{t-1} + K) - K
+                    inner = __builtin_fmaf(dv, ht + K, -(K * q));
                 } else {
                     const float x = x2 * kLn2;
                     const float ph = __builtin_fmaf(
@@ -332,11 +340,14 @@ struct Bwd {
         }
     }
 
+    // hp, ht: the states before and after the step (ht is read by FULL steps
+    // only).
     template <int SM, bool FULL>
     __device__ __forceinline__ void rev(float (&g)[kH], float (&dA)[kH], const float (&hp)[kH],
-                                        float uv, float dv, float dY, const float (&Bv)[kH],
-                                        const float (&Cv)[kH], const float (&av)[kH],
-                                        float& du_acc, float& ddv_acc, float (&dBp)[kH]) const {
+                                        const float (&ht)[kH], float uv, float dv, float dY,
+                                        const float (&Bv)[kH], const float (&Cv)[kH],
+                                        const float (&av)[kH], float& du_acc, float& ddv_acc,
+                                        float (&dBp)[kH]) const {
         const float udv = uv * dv;
 #pragma unroll
         for (int j = 0; j < kH; j++) {
@@ -345,11 +356,11 @@ struct Bwd {
                 continue;
             }
             if (slow_state<SM>(j))
-                rev_state<true, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
-                                      av[j], du_acc, ddv_acc, dBp[j]);
+                rev_state<true, FULL>(j, g[j], dA[j], hp[j], ht[j], uv, dv, udv, dY, Bv[j],
+                                      Cv[j], av[j], du_acc, ddv_acc, dBp[j]);
             else
-                rev_state<false, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j], Cv[j],
-                                       av[j], du_acc, ddv_acc, dBp[j]);
+                rev_state<false, FULL>(j, g[j], dA[j], hp[j], ht[j], uv, dv, udv, dY, Bv[j],
+                                       Cv[j], av[j], du_acc, ddv_acc, dBp[j]);
         }
     }
 
@@ -477,7 +488,7 @@ struct Bwd {
             if (i >= n) continue;
             float Cv[kH];
             read_row(32, i, Cv);
-            rev<SM, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
+            rev<SM, false>(g, dA, hp, hp, 0.0f, dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
         }
     }
 
@@ -516,11 +527,10 @@ struct Bwd {
                                           const float (&uu)[kT], const float (&dl)[kT],
                                           const float (&dv)[kT], const float (&go)[kT],
                                           const float (&zz)[kT], float* pB, float* pC) const {
-        float hist[kT][kH];
+        float hist[kT + 1][kH];   // hist[i]: the states before step i of the block
         float dY[kT];
-        float h[kH];
 #pragma unroll
-        for (int j = 0; j < kH; j++) h[j] = hist[0][j] = h_in[j];
+        for (int j = 0; j < kH; j++) hist[0][j] = h_in[j];
         const bool writer = live && half == 0;
         const bool red_writer = (threadIdx.x & 3u) == 0;
         const uint32_t n_out = half * kH + ((threadIdx.x & 31u) >> 2);
@@ -531,21 +541,21 @@ struct Bwd {
             float Bv[kH], Cv[kH], av[kH];
             read_row(0, i, Bv);
             read_row(32, i, Cv);
-            fwd<SM>(h, uu[i], dv[i], Bv, av);
+            fwd<SM>(hist[i], hist[i + 1], uu[i], dv[i], Bv, av);
+            const float (&h)[kH] = hist[i + 1];
             // aBar of the step, kept for the adjoint below (this lane only)
             acache[(i * 2) * kWave + threadIdx.x] = make_float4(av[0], av[1], av[2], av[3]);
             acache[(i * 2 + 1) * kWave + threadIdx.x] = make_float4(av[4], av[5], av[6], av[7]);
-            if (i + 1 < kT) {
-#pragma unroll
-                for (int j = 0; j < kH; j++) hist[i + 1][j] = h[j];
-            }
             float yp = 0.0f;
 #pragma unroll
             for (int j = 0; j < kH; j++) yp = __builtin_fmaf(Cv[j], h[j], yp);
             const float y = __builtin_fmaf(dvec, uu[i], pair_sum(yp));
-            dY[i] = grad_y(go[i], zz[i]);
+            // sigmoid(z) once for dY = dout SiLU(z) and for dz
+            const float sz = gated ? sigmoid(zz[i]) : 0.0f;
+            dY[i] = live ? (gated ? go[i] * (zz[i] * sz) : go[i]) : 0.0f;
             const int64_t r = row(s + i);
-            if (gated && writer) c.dz[r * D + d] = go[i] * y * silu_grad(zz[i]);
+            if (gated && writer)
+                c.dz[r * D + d] = go[i] * y * (sz * __builtin_fmaf(zz[i], 1.0f - sz, 1.0f));
             float dCp[kH];
 #pragma unroll
             for (int j = 0; j < kH; j++) dCp[j] = dY[i] * h[j];
@@ -563,7 +573,8 @@ struct Bwd {
             const float4 a_hi = acache[(i * 2 + 1) * kWave + threadIdx.x];
             const float av[kH] = {a_lo.x, a_lo.y, a_lo.z, a_lo.w, a_hi.x, a_hi.y, a_hi.z, a_hi.w};
             float du_acc = 0.0f, ddv_acc = 0.0f;
-            rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
+            rev<SM, true>(g, dA, hist[i], hist[i + 1], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc,
+                          ddv_acc, dBp);
             const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
             const float ddv = pair_sum(ddv_acc);
             const int64_t r = row(s + i);
