@@ -145,7 +145,7 @@ int cu_count() {
 mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const float* B,
                           const float* C, const float* z) {
     static const int64_t waves_per_cu = env_or("MSS_SCAN_WAVES_PER_CU", 8);
-    static const int64_t min_seg = env_or("MSS_SCAN_MIN_SEG", 512);
+    static const int64_t min_seg = env_or("MSS_SCAN_MIN_SEG", 64);
     mss::ScanShape s;
     s.B = dims->batch;
     s.L = dims->seq_len;
@@ -251,11 +251,11 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // Work split of the scan backward: the flattened (channel tile, t) space cut
 // into segments of equal length, about two waves per SIMD, but no segment
-// shorter than MSS_BWD_MIN_SEG steps (default 256), so that the two decay
-// replays of a segment stay a small fraction of its work.
+// shorter than MSS_BWD_MIN_SEG steps (default 64): below that the two decay
+// replays of a segment outweigh its own steps.
 mss::BwdShape bwd_shape(const mss_dims* dims) {
     static const int64_t waves_per_cu = env_or("MSS_BWD_WAVES_PER_CU", 8);
-    static const int64_t min_seg = env_or("MSS_BWD_MIN_SEG", 256);
+    static const int64_t min_seg = env_or("MSS_BWD_MIN_SEG", 64);
     mss::BwdShape s;
     s.B = dims->batch;
     s.L = dims->seq_len;

@@ -69,9 +69,11 @@ def test_core_infinite_delta_inside_a_replay_window(disc):
     """+Inf in delta a few steps before a segment start, so dv = +Inf lies
     inside the window the segment replays (its backward walk stops there) and
     the replay's remaining sum of dv is infinite; every state must still take
-    part in the replay.  This shape is cut into segments of 512 steps of the
-    flattened (column tile, t) space: row 1's tiles start segments at
-    t = 72, 584, 1096 (channels 0-63) and t = 108, 620, 1132 (64-99).  ZOH:
+    part in the replay.  This shape is cut into segments of 64 steps of the
+    flattened (column tile, t) space (the library's shortest segment): row
+    1's tiles start segments at every t = 8 (mod 64) for channels 0-63,
+    among them t = 584, and at every t = 44 (mod 64) for channels 64-99,
+    among them t = 620 and 1132.  ZOH:
     aBar = 0 resets the column there and every output stays finite; EULER:
     dv B u is infinite, the column is non-finite from there on.  Outputs are
     compared wherever the oracle is finite."""
