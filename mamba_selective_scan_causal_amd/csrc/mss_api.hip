@@ -584,10 +584,10 @@ int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float
     }
     // Segments: about five workgroups per CU (two are resident at a time;
     // the surplus evens out the finish), none shorter than MSS_SSD_MIN_SEG
-    // steps (default 512), so that the replay that rebuilds a segment's
-    // initial state stays a small share of its work.
+    // steps (default 64, two chunks), so that the replay that rebuilds a
+    // segment's initial state does not outweigh its own steps.
     static const int64_t wg_per_cu = env_or("MSS_SSD_WG_PER_CU", 5);
-    static const int64_t min_seg = env_or("MSS_SSD_MIN_SEG", 512);
+    static const int64_t min_seg = env_or("MSS_SSD_MIN_SEG", 64);
     const int64_t Q = mss::ssd_chunk_len();
     const int64_t nchunks = (L + Q - 1) / Q;
     const int64_t bh = Bt * H;
