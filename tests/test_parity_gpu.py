@@ -191,6 +191,34 @@ def test_decode_64_steps_sampled(disc):
     assert np.array_equal(got_cs, o_cs), "conv state after 64 steps"
 
 
+@pytest.mark.parametrize("disc", DISCS)
+def test_decode_groups_per_wave(disc):
+    """301 sequences x 5120 channels, 4 steps: an odd batch (the last group of
+    two rows has one live row) and more groups than waves per channel tile,
+    so waves take several groups and the last group slot fewer.  Every
+    column is checked against the oracle."""
+    import torch
+    w = gen.DECODE.with_(name="decode_b301", batch=301, seq_len=4)
+    inp = gen.generate(w)
+    S, B, D, N, K = w.seq_len, w.batch, w.d_inner, w.d_state, w.d_conv
+    d = {k: dev(v) for k, v in inp.items()}
+    h, cs = d["h"].clone(), d["conv_state"].clone()
+    o_h, o_cs = inp["h"].astype(np.float64), inp["conv_state"].astype(np.float64)
+    y = nan_like((B, D))
+    for s in range(S):
+        y.fill_(float("nan"))
+        mss.selective_step(d["x"][s], d["z"][s], d["delta"][s], d["A_log"], d["B"][s], d["C"][s],
+                           d["D_vec"], d["w_conv"], d["b_conv"], cs, h, disc=disc, out=y)
+        oy, o_cs, o_h = oracle.selective_step(inp["x"][s], inp["z"][s], inp["delta"][s],
+                                              inp["A_log"], inp["B"][s], inp["C"][s],
+                                              inp["D_vec"], inp["w_conv"], inp["b_conv"], o_cs,
+                                              o_h, disc=disc)
+        torch.cuda.synchronize()
+        assert_close(host(y), oy, f"y step {s}")
+    assert_close(host(h), o_h, "h")
+    assert np.array_equal(host(cs), o_cs), "conv state"
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 
