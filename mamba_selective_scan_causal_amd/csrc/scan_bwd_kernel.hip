@@ -33,7 +33,7 @@
 //      terms).
 // Cross-channel sums: each step's 8 dB (or dC) values per lane are reduced
 // over the 32 channels of the tile with a transpose-reduce (one exchange
-// level per lane bit, DPP and ds_swizzle), then written per tile to a
+// level per lane bit: row swap, DPP), then written per tile to a
 // partial buffer that a second kernel sums over tiles in a fixed order; dA
 // and dD are written per piece and summed the same way.  No atomics: the
 // result is bitwise reproducible.
@@ -74,11 +74,10 @@ struct BwdCols {
 
 __device__ __forceinline__ float as_f(int v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ int as_i(float v) { return __builtin_bit_cast(int, v); }
+__device__ __forceinline__ uint32_t as_u(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float u_as_f(uint32_t v) { return __builtin_bit_cast(float, v); }
 
 // Lane exchanges inside a 32-lane half.
-__device__ __forceinline__ float xor16(float v) {   // ds_swizzle, bit mode: and 0x1f, xor 0x10
-    return as_f(__builtin_amdgcn_ds_swizzle(as_i(v), 0x401f));
-}
 __device__ __forceinline__ float xor8(float v) {    // DPP row_ror:8 (rotation by 8 in 16 lanes)
     return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0x128, 0xf, 0xf, true));
 }
@@ -91,28 +90,48 @@ __device__ __forceinline__ float xor2(float v) {    // DPP quad_perm [2,3,0,1]
 __device__ __forceinline__ float xor1(float v) {    // DPP quad_perm [1,0,3,2]
     return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0xb1, 0xf, 0xf, true));
 }
-// Sum of the two halves of a channel (lanes l and l ^ 32).
-__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32); }
 
-// Sum over the 32 lanes of this half of v[j], for j = q >> 2 (q = lane & 31):
-// three exchange levels that each keep half of the values (selected by lane
-// bits 4, 3, 2) and add the partner's other half, then two plain levels.
+// gfx950's v_permlane16_swap trades the odd 16-lane rows of its first
+// operand for the even rows of its second.  With x, y in every lane this
+// leaves x's rows (0, 0, 2, 2) and y's rows (1, 1, 3, 3) behind, so the sum
+// of the two results is, in lanes with bit 4 clear, x plus x of lane + 16,
+// and in lanes with bit 4 set, y plus y of lane - 16 (lower lane first in
+// both).  (Both results are copied out before use.)
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(y), false, false);
+    const uint32_t nx = r[0], ny = r[1];
+    return u_as_f(nx) + u_as_f(ny);
+}
+
+// Sum of the two halves of a channel (lanes l and l ^ 32): v_permlane32_swap
+// of v with itself leaves the lower half of v in both halves of one result
+// and the upper half in both halves of the other.
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return u_as_f(lo) + u_as_f(hi);
+}
+
+// Sum over the 32 lanes of this half of v[j], for j = 4 b3 + 2 b4 + b2
+// (b4, b3, b2: bits 4, 3, 2 of the lane): three exchange levels that each
+// keep half of the values and add the partner's other half -- lane bit 4
+// with register bit 1 (the row swap above), lane bit 3 with register bit 2,
+// lane bit 2 with register bit 0 -- then two plain levels.
 __device__ __forceinline__ float reduce8(const float (&v)[kH]) {
     const uint32_t q = threadIdx.x & 31u;
-    const bool b4 = q & 16u, b3 = q & 8u, b2 = q & 4u;
-    float w4[4];
+    const bool b3 = q & 8u, b2 = q & 4u;
+    float w4[4];   // w4[2 r2 + r0]: register 4 r2 + 2 b4 + r0
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float keep = b4 ? v[i + 4] : v[i];
-        const float send = b4 ? v[i] : v[i + 4];
-        w4[i] = keep + xor16(send);
-    }
-    float w2[2];
+    for (int r2 = 0; r2 < 2; r2++)
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const float keep = b3 ? w4[i + 2] : w4[i];
-        const float send = b3 ? w4[i] : w4[i + 2];
-        w2[i] = keep + xor8(send);
+        for (int r0 = 0; r0 < 2; r0++)
+            w4[2 * r2 + r0] = swap16_sum(v[4 * r2 + r0], v[4 * r2 + 2 + r0]);
+    float w2[2];   // w2[r0]: register 4 b3 + 2 b4 + r0
+#pragma unroll
+    for (int r0 = 0; r0 < 2; r0++) {
+        const float keep = b3 ? w4[2 + r0] : w4[r0];
+        const float send = b3 ? w4[r0] : w4[2 + r0];
+        w2[r0] = keep + xor8(send);
     }
     const float keep = b2 ? w2[1] : w2[0];
     const float send = b2 ? w2[0] : w2[1];
@@ -120,6 +139,12 @@ __device__ __forceinline__ float reduce8(const float (&v)[kH]) {
     w1 += xor2(w1);
     w1 += xor1(w1);
     return w1;
+}
+
+// State (within the lane's half) whose sum reduce8 leaves in this lane.
+__device__ __forceinline__ uint32_t reduce8_state() {
+    const uint32_t q = threadIdx.x & 31u;
+    return ((q >> 1) & 4u) | ((q >> 3) & 2u) | ((q >> 2) & 1u);
 }
 
 // sigmoid(v); SiLU(v) = v sigmoid(v) and d SiLU / dv = s (1 + v (1 - s)) with
@@ -533,7 +558,7 @@ struct Bwd {
         for (int j = 0; j < kH; j++) hist[0][j] = h_in[j];
         const bool writer = live && half == 0;
         const bool red_writer = (threadIdx.x & 3u) == 0;
-        const uint32_t n_out = half * kH + ((threadIdx.x & 31u) >> 2);
+        const uint32_t n_out = half * kH + reduce8_state();
         // Recompute the block's states (forward), with dz and the dC terms.
 #pragma unroll
         for (int i = 0; i < kT; i++) {
