@@ -299,6 +299,7 @@ struct Bwd {
 
     // ---- reverse (adjoint) step ------------------------------------------
     // FULL: also the gradient terms (du, ddv, dA, dB); otherwise only g.
+    // du_acc and ddv_acc are this lane's sums over its states for the step.
     // With dh = C dY + g and gn = aBar dh (the adjoint passed to step t-1):
     //   ZOH (q = (aBar-1)/A, K = u B / A):
     //     du += dh q B,  dB term = dh q u,  ddv += gn (h_{t-1} A + u B),
@@ -312,8 +313,7 @@ struct Bwd {
     // FULL steps take aBar from the block's recompute (a_in); the replay
     // computes it.
     template <bool SLOW, bool FULL>
-    __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float ht,
-                                              float uv, float dv, float udv, float dY, float Bj,
+    __device__ __forceinline__ void rev_state(int j, float& g, float& dA, float hp, float uv, float dv, float udv, float dY, float Bj,
                                               float Cj, float a_in, float& du_acc,
                                               float& ddv_acc, float& dBp) const {
         const float x2 = (SLOW || !FULL) ? dv * A2[j] : 0.0f;
@@ -339,37 +339,39 @@ struct Bwd {
                 dBp = dq * uv;
                 const float uB = uv * Bj;
                 const float K = uB * Ai[j];
-                ddv_acc = __builtin_fmaf(gn, __builtin_fmaf(hp, An[j], uB), ddv_acc);
-                float inner;
                 if constexpr (!SLOW) {
-                    // aBar (h_{t-1} + K) = h_t + K on the fast path, whose
-                    // update is h_t = aBar (h_{t-1} + K) - K
-                    inner = __builtin_fmaf(dv, ht + K, -(K * q));
+                    // with X = gn (h_{t-1} + K) = dh aBar (h_{t-1} + K) the
+                    // ddv term gn (h_{t-1} A + u B) is A X and the dA term
+                    // dv X - dh q K
+                    const float X = gn * (hp + K);
+                    ddv_acc = __builtin_fmaf(X, An[j], ddv_acc);
+                    dA = __builtin_fmaf(-dq, K, __builtin_fmaf(dv, X, dA));
                 } else {
+                    ddv_acc = __builtin_fmaf(gn, __builtin_fmaf(hp, An[j], uB), ddv_acc);
                     const float x = x2 * kLn2;
                     const float ph = __builtin_fmaf(
                         x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f),
                         0.5f);
                     const float t5d = __builtin_fmaf(dv, a, -q);
                     const float t5 = __builtin_fabsf(x) < kSmallX ? (dv * x) * ph : t5d;
-                    inner = __builtin_fmaf(dv * a, hp, K * t5);
+                    dA = __builtin_fmaf(dh, __builtin_fmaf(dv * a, hp, K * t5), dA);
                 }
-                dA = __builtin_fmaf(dh, inner, dA);
             } else {
-                du_acc = __builtin_fmaf(dh, dv * Bj, du_acc);
+                // du_acc collects sum_n dh B here; rev scales it by dv (du)
+                // and by u (its ddv part) after the last state
+                du_acc = __builtin_fmaf(dh, Bj, du_acc);
                 dBp = dh * udv;
-                ddv_acc = __builtin_fmaf(gn, hp * An[j], ddv_acc);
-                ddv_acc = __builtin_fmaf(dh, uv * Bj, ddv_acc);
-                dA = __builtin_fmaf(gn, dv * hp, dA);
+                const float gh = gn * hp;
+                ddv_acc = __builtin_fmaf(gh, An[j], ddv_acc);
+                dA = __builtin_fmaf(gh, dv, dA);
             }
         }
     }
 
-    // hp, ht: the states before and after the step (ht is read by FULL steps
-    // only).
+    // hp: the states before the step.
     template <int SM, bool FULL>
     __device__ __forceinline__ void rev(float (&g)[kH], float (&dA)[kH], const float (&hp)[kH],
-                                        const float (&ht)[kH], float uv, float dv, float dY,
+                                        float uv, float dv, float dY,
                                         const float (&Bv)[kH], const float (&Cv)[kH],
                                         const float (&av)[kH], float& du_acc, float& ddv_acc,
                                         float (&dBp)[kH]) const {
@@ -381,11 +383,15 @@ struct Bwd {
                 continue;
             }
             if (slow_state<SM>(j))
-                rev_state<true, FULL>(j, g[j], dA[j], hp[j], ht[j], uv, dv, udv, dY, Bv[j],
+                rev_state<true, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j],
                                       Cv[j], av[j], du_acc, ddv_acc, dBp[j]);
             else
-                rev_state<false, FULL>(j, g[j], dA[j], hp[j], ht[j], uv, dv, udv, dY, Bv[j],
+                rev_state<false, FULL>(j, g[j], dA[j], hp[j], uv, dv, udv, dY, Bv[j],
                                        Cv[j], av[j], du_acc, ddv_acc, dBp[j]);
+        }
+        if constexpr (FULL && !kZoh) {
+            ddv_acc = __builtin_fmaf(uv, du_acc, ddv_acc);
+            du_acc *= dv;
         }
     }
 
@@ -513,7 +519,7 @@ struct Bwd {
             if (i >= n) continue;
             float Cv[kH];
             read_row(32, i, Cv);
-            rev<SM, false>(g, dA, hp, hp, 0.0f, dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
+            rev<SM, false>(g, dA, hp, 0.0f, dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
         }
     }
 
@@ -598,8 +604,7 @@ struct Bwd {
             const float4 a_hi = acache[(i * 2 + 1) * kWave + threadIdx.x];
             const float av[kH] = {a_lo.x, a_lo.y, a_lo.z, a_lo.w, a_hi.x, a_hi.y, a_hi.z, a_hi.w};
             float du_acc = 0.0f, ddv_acc = 0.0f;
-            rev<SM, true>(g, dA, hist[i], hist[i + 1], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc,
-                          ddv_acc, dBp);
+            rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
             const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
             const float ddv = pair_sum(ddv_acc);
             const int64_t r = row(s + i);

@@ -11,3 +11,5 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    import gpu_util
+    gpu_util._capture = config.pluginmanager.getplugin("capturemanager")

@@ -8,10 +8,22 @@ import numpy as np
 TOL = 1e-4  # max relative error, fp32 GPU vs fp64 oracle
 
 
+# pytest's capture manager, set by conftest.pytest_configure: announce
+# suspends capture through it so the line reaches the real stderr at once.
+_capture = None
+
+
 def announce(msg: str):
-    """Print a progress line that survives pytest's capture and a dying process."""
-    sys.__stderr__.write(f"[gpu] {msg}\n")
-    sys.__stderr__.flush()
+    """Print a progress line to the terminal's stderr, flushed, with pytest's
+    output capture suspended, so it shows even when the test passes or the
+    process dies in the next GPU call."""
+    if _capture is not None:
+        with _capture.global_and_fixture_disabled():
+            sys.stderr.write(f"[gpu] {msg}\n")
+            sys.stderr.flush()
+    else:
+        sys.stderr.write(f"[gpu] {msg}\n")
+        sys.stderr.flush()
 
 
 def dev(a):
