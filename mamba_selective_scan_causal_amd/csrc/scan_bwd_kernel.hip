@@ -733,12 +733,28 @@ __device__ __forceinline__ int64_t tile_pieces(const BwdShape& s, int64_t ti) {
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdCols c, BwdShape s, float* dB,
                                                          float* dC, float* dA_log, float* dD) {
     const int64_t M = s.B * s.L;
-    const int64_t nBC = M * s.N;
+    // dB/dC items: four states (one 16-byte piece of a row) each when N = 16,
+    // else one state each
+    const bool vec = s.N == 16;
+    const int64_t nBC = vec ? M * 4 : M * s.N;
     const int64_t nA = s.D * s.N;
     const int64_t total = nBC + nA + (dD ? s.D : 0);
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        if (i < nBC) {
+        if (i < nBC && vec) {
+            const int64_t r = i >> 2, n0 = (i & 3) * 4;
+            const int64_t b = r / s.L, t = r - b * s.L;
+            float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
+            for (int64_t ct = 0; ct < s.tiles_per_b; ct++) {
+                const int64_t o = ((b * s.tiles_per_b + ct) * s.L + t) * 16 + n0;
+                const float4 pb = *reinterpret_cast<const float4*>(c.partB + o);
+                const float4 pc = *reinterpret_cast<const float4*>(c.partC + o);
+                sb.x += pb.x; sb.y += pb.y; sb.z += pb.z; sb.w += pb.w;
+                sc.x += pc.x; sc.y += pc.y; sc.z += pc.z; sc.w += pc.w;
+            }
+            *reinterpret_cast<float4*>(dB + r * 16 + n0) = sb;
+            *reinterpret_cast<float4*>(dC + r * 16 + n0) = sc;
+        } else if (i < nBC) {
             const int64_t r = i / s.N, n = i - r * s.N;
             const int64_t b = r / s.L, t = r - b * s.L;
             float sb = 0.0f, sc = 0.0f;
@@ -796,7 +812,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a, const BwdShape& s, hipStream_t st) 
     else
         e = vec ? launch_t<MSS_DISC_ZOH, 16>(c, s, st) : launch_t<MSS_DISC_ZOH, 0>(c, s, st);
     if (e != hipSuccess) return e;
-    const int64_t total = s.B * s.L * s.N + s.D * s.N + (a.dD_vec ? s.D : 0);
+    const int64_t total = s.B * s.L * (s.N == 16 ? 4 : s.N) + s.D * s.N + (a.dD_vec ? s.D : 0);
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
