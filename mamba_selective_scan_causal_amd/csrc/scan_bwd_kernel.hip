@@ -112,6 +112,15 @@ __device__ __forceinline__ float pair_sum(float v) {
     return u_as_f(lo) + u_as_f(hi);
 }
 
+// The channel sums of two values at once: the swap of a with b leaves
+// (a, b) of the lower half in one result and (a, b) of the upper half in the
+// other, so lanes 0-31 get a_l + a_{l+32} and lanes 32-63 b_{l-32} + b_l.
+__device__ __forceinline__ float pair_sum2(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u(a), as_u(b), false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return u_as_f(lo) + u_as_f(hi);
+}
+
 // Sum over the 32 lanes of this half of v[j], for j = 4 b3 + 2 b4 + b2
 // (b4, b3, b2: bits 4, 3, 2 of the lane): three exchange levels that each
 // keep half of the values and add the partner's other half -- lane bit 4
@@ -605,13 +614,11 @@ struct Bwd {
             const float av[kH] = {a_lo.x, a_lo.y, a_lo.z, a_lo.w, a_hi.x, a_hi.y, a_hi.z, a_hi.w};
             float du_acc = 0.0f, ddv_acc = 0.0f;
             rev<SM, true>(g, dA, hist[i], uu[i], dv[i], dY[i], Bv, Cv, av, du_acc, ddv_acc, dBp);
-            const float duv = __builtin_fmaf(dY[i], dvec, pair_sum(du_acc));
-            const float ddv = pair_sum(ddv_acc);
-            const int64_t r = row(s + i);
-            if (writer) {
-                c.du[r * D + d] = duv;
-                c.ddelta[r * D + d] = ddv * sigmoid(dl[i]);
-            }
+            // the lower half stores du, the upper half ddelta (same channel)
+            const float sum = pair_sum2(du_acc, ddv_acc);
+            const float val = half == 0 ? __builtin_fmaf(dY[i], dvec, sum) : sum * sigmoid(dl[i]);
+            float* dst = half == 0 ? c.du : c.ddelta;
+            if (live) dst[row(s + i) * D + d] = val;
             dD = __builtin_fmaf(dY[i], uu[i], dD);
             const float sB = reduce8(dBp);
             if (red_writer) pB[(s + i) * 16 + n_out] = sB;
