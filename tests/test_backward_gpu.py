@@ -89,13 +89,15 @@ def test_scan_backward_workloads(w, disc):
     check_all(run_bwd(inp, w, disc), oracle_bwd(inp, w, disc))
 
 
-def test_scan_backward_full_size():
-    """B4 L8192 D5120 N16, ZOH, gated, in the launch configuration bench.py
-    times: every gradient against the oracle run on the whole problem."""
+@pytest.mark.parametrize("disc", DISCS)
+def test_scan_backward_full_size(disc):
+    """B4 L8192 D5120 N16, gated, in the launch configuration bench.py times
+    (ZOH there; EULER through the same split): every gradient against the
+    oracle run on the whole problem."""
     w = gen.MAMBA_2P8B
     inp = _scan_inputs(w)
-    got = run_bwd(inp, w, "zoh", h0=False)
-    want = oracle_bwd(inp, w, "zoh", h0=False)
+    got = run_bwd(inp, w, disc, h0=False)
+    want = oracle_bwd(inp, w, disc, h0=False)
     check_all(got, want)
 
 
