@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 1
+#define MSS_VERSION 2
 
 /* Status codes. */
 #define MSS_OK 0
@@ -58,10 +58,38 @@ extern "C" {
 #define MSS_EHIP (-5)       /* a HIP runtime call or kernel launch failed; see mss_last_hip_error */
 
 /* Problem sizes.  `struct_size` must be sizeof(mss_dims): it guards against a
- * caller built against a different layout of this struct. */
+ * caller built against a different layout of this struct.
+ *
+ * Time split.  The recurrence of every (b, d) column runs sequentially in
+ * time, and a Mamba-1 problem has few enough columns that the scans split
+ * time into segments processed in parallel.  A segment that starts at
+ * t0 > 0 rebuilds the state it starts from, h(t0-1), by replaying the
+ * recurrence from h = 0 over a window [tw, t0): tw is the latest step from
+ * which every state of the segment's columns has decayed by at least
+ * 2^-MSS_REPLAY_DECAY_BITS (prod aBar = exp(A sum dv), decided from delta
+ * alone), or tw = 0.  (A state that decays faster than the slowest one
+ * joins the replay later, at the 8-step block from which its own decay
+ * reaches the same bound.)  Relative to the plain sequential recurrence the
+ * state at t >= t0 then lacks exactly
+ *     prod_{s=tj..t} aBar_s[n] * h_{tj-1}[n]   <=   2^-MSS_REPLAY_DECAY_BITS |h_{tj-1}[n]|
+ * per state n, where tj is the step its replay started from, and an output
+ * y_t lacks sum_n C_t[n] times that (times SiLU(z_t)).  So the difference
+ * from the sequential recurrence is bounded by 2^-MSS_REPLAY_DECAY_BITS
+ * times the magnitude of the state at the replay start: only a state far
+ * above the scale of the outputs shortly before a segment start could make
+ * it visible.  Segment lengths depend on the shape (and flags) alone, never
+ * on the device or the environment: mss_time_split reports them, and the
+ * output bits are a function of the inputs and the shape.
+ * MSS_FLAG_EXACT turns the split off: each channel tile scans its whole
+ * sequence in one wave, so there is no replay and the result is the plain
+ * recurrence in fp32, at the cost of parallelism (B * ceil(D/64) waves for
+ * the scans, B * ceil(D/32) for the scan backward, B * H workgroups for the
+ * SSD scan). */
+#define MSS_REPLAY_DECAY_BITS 24
+#define MSS_FLAG_EXACT 1
 typedef struct mss_dims {
     int32_t struct_size;
-    int32_t reserved;       /* must be 0 */
+    int32_t flags;          /* 0, or MSS_FLAG_EXACT (any other bit: MSS_EINVAL) */
     int64_t batch;          /* B */
     int64_t seq_len;        /* L (ignored by mss_selective_step) */
     int64_t d_inner;        /* D */
@@ -96,10 +124,8 @@ int mss_conv1d_silu(const mss_dims* dims, const float* x, const float* w_conv,
  *   h0, h_last (B, D, N);  h_cache (B, L, D, N) = h_t after the update of step t.
  *   Optional (NULL allowed): D_vec (= 0), z (ungated output), h0 (= 0),
  *   h_cache, h_last.  Required: u, delta, A_log, B, C, y.
- *   Time is split into segments processed in parallel; a segment starting
- *   at t0 > 0 rebuilds h(t0-1) by replaying the recurrence from h = 0 at the
- *   step where every lane's slowest state has decayed by 2^-24 (or from
- *   t = 0), so it drops contributions that have decayed by more than 2^-24;
+ *   Time is split into segments processed in parallel (see "Time split"
+ *   above for what that drops, and MSS_FLAG_EXACT for the path without it);
  *   the result is otherwise the plain recurrence in fp32.                  */
 int mss_selective_scan(const mss_dims* dims, int disc, const float* u, const float* delta,
                        const float* A_log, const float* B, const float* C, const float* D_vec,
@@ -198,8 +224,11 @@ int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes);
  *   dD_vec (D)     = sum_{b,t} dY u                 (NULL: not computed)
  *   dz (M, D)      = dout y SiLU'(z), y ungated     (required iff z given)
  *   dh0 (B, D, N)  = the adjoint after step 0       (NULL: not computed)
- * The adjoint carried between time segments processed in parallel drops
- * contributions that have decayed by more than 2^-24, as in the forward.  */
+ * Time segments are processed in parallel as in the forward: each rebuilds
+ * the forward state entering it and the adjoint leaving it by replays whose
+ * starting point has decayed by 2^-MSS_REPLAY_DECAY_BITS (see "Time split";
+ * for the adjoint the window runs forward in time from the segment end).
+ * MSS_FLAG_EXACT: no split, no replay.                                      */
 int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 const float* delta, const float* A_log, const float* B,
                                 const float* C, const float* D_vec, const float* z,
@@ -229,11 +258,13 @@ int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* 
  *   y[r, h*P + p] = sum_n C[r, g*N + n] S_h[p, n] + D_vec[h] x[r, h*P + p]
  * with f = dv (MSS_DISC_EULER, the Mamba-2 form) or expm1(dv A_h) / A_h
  * (MSS_DISC_ZOH, the discretisation of the pages' Mamba-1 path).
- * Computed in chunks on the matrix cores (fp32 MFMA); segments processed in
- * parallel drop contributions that have decayed by more than 2^-24. */
+ * Computed in chunks on the matrix cores (fp32 MFMA); time segments are
+ * processed in parallel, each rebuilding its initial state by a replay whose
+ * start has decayed by 2^-MSS_REPLAY_DECAY_BITS (see "Time split"; here the
+ * decay is the head's scalar exp(A_h sum dv)).  MSS_FLAG_EXACT: no split. */
 typedef struct mss_ssd_dims {
     int32_t struct_size;    /* sizeof(mss_ssd_dims) */
-    int32_t reserved;       /* must be 0 */
+    int32_t flags;          /* 0, or MSS_FLAG_EXACT (any other bit: MSS_EINVAL) */
     int64_t batch;          /* B */
     int64_t seq_len;        /* L */
     int64_t n_heads;        /* H */
@@ -249,6 +280,22 @@ typedef struct mss_ssd_dims {
 int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float* dt, const float* A_log,
                  const float* B, const float* C, const float* D_vec, const float* dt_bias,
                  const float* h0, float* y, float* h_last, hipStream_t stream);
+
+/* ---- Time split ----------------------------------------------------------
+ * The segment length, in steps, that a call with these dims (flags
+ * included) uses, for callers and tests that need to know where segments
+ * start.  op: MSS_OP_SELECTIVE_SCAN (mss_selective_scan, mss_mamba1_core and
+ * their strided forms) or MSS_OP_SELECTIVE_SCAN_BACKWARD.  The scans cut the
+ * flattened (tile, t) space, tile = b * ceil(D/T) + d / T with T = 64
+ * channels (forward) or 32 (backward) and t running fastest, into pieces of
+ * *segment_steps steps; a segment starts wherever (tile * L + t) is a
+ * multiple of *segment_steps.  0 for empty problems.                        */
+#define MSS_OP_SELECTIVE_SCAN 3
+int mss_time_split(const mss_dims* dims, int op, int64_t* segment_steps);
+
+/* The same for mss_ssd_scan: every (batch row, head) sequence is cut into
+ * segments of *segment_steps steps starting at t = 0.                       */
+int mss_ssd_time_split(const mss_ssd_dims* dims, int64_t* segment_steps);
 
 /* Human-readable text for a status code (static storage). */
 const char* mss_strerror(int status);

@@ -38,14 +38,18 @@ class MssError(RuntimeError):
 
 
 class Dims(ctypes.Structure):
-    _fields_ = [("struct_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("struct_size", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
                 ("d_conv", ctypes.c_int64)]
 
 
-def make_dims(batch, seq_len, d_inner, d_state, d_conv=1) -> Dims:
-    return Dims(ctypes.sizeof(Dims), 0, batch, seq_len, d_inner, d_state, d_conv)
+FLAG_EXACT = 1          # no time split: the plain sequential recurrence
+
+
+def make_dims(batch, seq_len, d_inner, d_state, d_conv=1, exact=False) -> Dims:
+    return Dims(ctypes.sizeof(Dims), FLAG_EXACT if exact else 0, batch, seq_len, d_inner,
+                d_state, d_conv)
 
 
 class Strides(ctypes.Structure):
@@ -59,25 +63,26 @@ def make_strides(x, z, delta, B, C, y) -> Strides:
 
 
 class SsdDims(ctypes.Structure):
-    _fields_ = [("struct_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("struct_size", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
                 ("d_state", ctypes.c_int64), ("n_groups", ctypes.c_int64)]
 
 
-def make_ssd_dims(batch, seq_len, n_heads, head_dim, d_state, n_groups=1) -> SsdDims:
-    return SsdDims(ctypes.sizeof(SsdDims), 0, batch, seq_len, n_heads, head_dim, d_state,
-                   n_groups)
+def make_ssd_dims(batch, seq_len, n_heads, head_dim, d_state, n_groups=1, exact=False) -> SsdDims:
+    return SsdDims(ctypes.sizeof(SsdDims), FLAG_EXACT if exact else 0, batch, seq_len, n_heads,
+                   head_dim, d_state, n_groups)
 
 
 EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_selective_step",
            "mss_selective_scan_strided", "mss_mamba1_core_strided",
            "mss_workspace_bytes", "mss_selective_scan_backward", "mss_conv1d_silu_backward",
-           "mss_ssd_scan",
+           "mss_ssd_scan", "mss_time_split", "mss_ssd_time_split",
            "mss_strerror", "mss_version", "mss_last_hip_error")
 
 OP_SELECTIVE_SCAN_BACKWARD = 1
 OP_CONV1D_SILU_BACKWARD = 2
+OP_SELECTIVE_SCAN = 3
 
 _lib = None
 
@@ -86,6 +91,11 @@ def lib():
     """The loaded libmss (ctypes).  Raises if the HIP library is not built."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime (soname libamdhip64.so.7, file name
+        # libamdhip64.so).  Loaded first, it also serves libmss's dependency;
+        # loading libmss first would bring in a second runtime from the ROCm
+        # install, which does not see torch's device memory.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m mamba_selective_scan_causal_amd.build`")
@@ -104,10 +114,13 @@ def lib():
         L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
         L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
         L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims), i] + [p] * 11
+        L.mss_time_split.argtypes = [dp, i, ctypes.POINTER(ctypes.c_int64)]
+        L.mss_ssd_time_split.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_int64)]
         for f in ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core",
                   "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
                   "mss_workspace_bytes", "mss_selective_scan_backward",
-                  "mss_conv1d_silu_backward", "mss_ssd_scan", "mss_version",
+                  "mss_conv1d_silu_backward", "mss_ssd_scan", "mss_time_split",
+                  "mss_ssd_time_split", "mss_version",
                   "mss_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         L.mss_strerror.argtypes = [ctypes.c_int]
@@ -220,15 +233,16 @@ def _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last):
 
 
 def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch, seq_len, disc,
-                   h_cache=False, h_last=False, out=None, stream=None):
+                   h_cache=False, h_last=False, out=None, stream=None, exact=False):
     """Selective scan + gate on a given u.  Returns (y, h_cache, h_last).
 
     ``h_cache`` / ``h_last``: False (skip), True (allocate) or an output tensor.
-    u, delta, z, B, C and ``out`` may be row-strided views (column slices)."""
+    u, delta, z, B, C and ``out`` may be row-strided views (column slices).
+    ``exact``: no time split (the plain sequential recurrence, less parallel)."""
     D, N = A_log.shape
     M = batch * seq_len
     y, hc, hl = _scan_outputs(u, batch, seq_len, D, N, out, h_cache, h_last)
-    dims = make_dims(batch, seq_len, D, N, 1)
+    dims = make_dims(batch, seq_len, D, N, 1, exact)
     common = (_ptr(A_log, "A_log", (D, N)),)
     tail = (_ptr(D_vec, "D_vec", (D,), False),)
     if _dense(u, delta, B, C, z, y):
@@ -255,15 +269,16 @@ def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
 
 
 def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
-                seq_len, disc, h_cache=False, h_last=False, out=None, stream=None):
+                seq_len, disc, h_cache=False, h_last=False, out=None, stream=None, exact=False):
     """Fused conv1d + SiLU + selective scan + gate from x.  Returns (y, h_cache, h_last).
 
-    x, delta, z, B, C and ``out`` may be row-strided views (column slices)."""
+    x, delta, z, B, C and ``out`` may be row-strided views (column slices).
+    ``exact``: no time split (the plain sequential recurrence, less parallel)."""
     D, N = A_log.shape
     K = w_conv.shape[1]
     M = batch * seq_len
     y, hc, hl = _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last)
-    dims = make_dims(batch, seq_len, D, N, K)
+    dims = make_dims(batch, seq_len, D, N, K, exact)
     conv = (_ptr(w_conv, "w_conv", (D, K)), _ptr(b_conv, "b_conv", (D,), False))
     if _dense(x, delta, B, C, z, y):
         _check("mss_mamba1_core", lib().mss_mamba1_core(
@@ -309,9 +324,9 @@ def selective_step(x, z, delta, A_log, B, C, D_vec, w_conv, b_conv, conv_state, 
     return y
 
 
-def workspace_bytes(op, *, batch, seq_len, d_inner, d_state, d_conv=1) -> int:
+def workspace_bytes(op, *, batch, seq_len, d_inner, d_state, d_conv=1, exact=False) -> int:
     """Workspace bytes a backward entry point needs (``op``: OP_* constant)."""
-    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv)
+    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv, exact)
     n = ctypes.c_size_t(0)
     _check("mss_workspace_bytes", lib().mss_workspace_bytes(ctypes.byref(dims), op,
                                                              ctypes.byref(n)))
@@ -339,15 +354,33 @@ def _workspace(op, like, workspace, stream, **dims):
     return base + pad, max(0, workspace.numel() - pad), workspace
 
 
+def time_split(op, *, batch, seq_len, d_inner, d_state, d_conv=1, exact=False) -> int:
+    """Segment length in steps of the flattened (channel tile, t) space that
+    ``op`` (OP_SELECTIVE_SCAN or OP_SELECTIVE_SCAN_BACKWARD) uses."""
+    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv, exact)
+    n = ctypes.c_int64(0)
+    _check("mss_time_split", lib().mss_time_split(ctypes.byref(dims), op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssd_time_split(*, batch, seq_len, n_heads, head_dim, d_state, n_groups=1,
+                   exact=False) -> int:
+    """Segment length in steps of every (batch row, head) sequence of ssd_scan."""
+    dims = make_ssd_dims(batch, seq_len, n_heads, head_dim, d_state, n_groups, exact)
+    n = ctypes.c_int64(0)
+    _check("mss_ssd_time_split", lib().mss_ssd_time_split(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
 def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch, seq_len, disc,
-                            need_dh0=False, workspace=None, stream=None):
+                            need_dh0=False, workspace=None, stream=None, exact=False):
     """Gradients of ``selective_scan``'s output against ``dout`` (batch*seq_len, D).
 
     Returns a dict: du, ddelta (M, D); dA_log (D, N); dB, dC (M, N);
     dD (D,) or None when D_vec is None; dz (M, D) or None when z is None;
     dh0 (batch, D, N) when ``need_dh0``.  ``workspace``: optional uint8 GPU
     tensor of at least ``workspace_bytes(OP_SELECTIVE_SCAN_BACKWARD, ...)``
-    + 256 bytes (allocated here when omitted).
+    + 256 bytes (allocated here when omitted).  ``exact``: no time split.
     """
     D, N = A_log.shape
     M = batch * seq_len
@@ -357,8 +390,8 @@ def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
          "dz": _empty((M, D), u) if z is not None else None,
          "dh0": _empty((batch, D, N), u) if need_dh0 else None}
     wp, wn, _keep = _workspace(OP_SELECTIVE_SCAN_BACKWARD, u, workspace, stream, batch=batch,
-                               seq_len=seq_len, d_inner=D, d_state=N)
-    dims = make_dims(batch, seq_len, D, N)
+                               seq_len=seq_len, d_inner=D, d_state=N, exact=exact)
+    dims = make_dims(batch, seq_len, D, N, 1, exact)
     _check("mss_selective_scan_backward", lib().mss_selective_scan_backward(
         ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
         _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
@@ -388,16 +421,18 @@ def conv1d_silu_backward(x, w_conv, b_conv, du, *, batch, seq_len, workspace=Non
 
 
 def ssd_scan(x, dt, A_log, B, C, D_vec=None, dt_bias=None, h0=None, *, batch, seq_len,
-             head_dim, d_state, n_groups=1, disc, h_last=False, out=None, stream=None):
+             head_dim, d_state, n_groups=1, disc, h_last=False, out=None, stream=None,
+             exact=False):
     """Mamba-2 SSD scan: y (batch*seq_len, H*head_dim) and, when ``h_last`` is
-    True (or a tensor), the final state (batch, H, head_dim, d_state)."""
+    True (or a tensor), the final state (batch, H, head_dim, d_state).
+    ``exact``: no time split."""
     H = A_log.shape[0]
     P, N, G = head_dim, d_state, n_groups
     M = batch * seq_len
     y = out if out is not None else _empty((M, H * P), x)
     hl = (h_last if not isinstance(h_last, bool) else
           (_empty((batch, H, P, N), x) if h_last else None))
-    dims = make_ssd_dims(batch, seq_len, H, P, N, G)
+    dims = make_ssd_dims(batch, seq_len, H, P, N, G, exact)
     _check("mss_ssd_scan", lib().mss_ssd_scan(
         ctypes.byref(dims), _disc(disc), _ptr(x, "x", (M, H * P)), _ptr(dt, "dt", (M, H)),
         _ptr(A_log, "A_log", (H,)), _ptr(B, "B", (M, G * N)), _ptr(C, "C", (M, G * N)),

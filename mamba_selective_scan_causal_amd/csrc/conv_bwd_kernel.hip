@@ -12,7 +12,8 @@
 // use, recomputing c from x (and dc over the K-1 steps past the run that dx
 // needs).  The dw / db sums stay in registers across all runs of the wave
 // and are written once per wave; a second kernel adds the waves of a channel
-// tile in a fixed order.
+// tile in a fixed order.  Each tap count 1..8 is its own instantiation, so
+// no padded zero tap multiplies an input (0 * Inf would be NaN).
 #include "device_math.h"
 #include "launch_bwd.h"
 
@@ -27,10 +28,9 @@ __device__ __forceinline__ float silu_grad(float v) {
     return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
 }
 
-template <int KS>
+template <int K>
 __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
-    constexpr int KR = KS > 0 ? KS : kMaxK;
-    const int K = KS > 0 ? KS : a.K;
+    constexpr int KR = K;
     const int64_t L = a.L, D = a.D;
     const int64_t runs = (L + kRun - 1) / kRun;
     const int64_t tile = blockIdx.x / a.groups;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
 
     float w[KR];
 #pragma unroll
-    for (int k = 0; k < KR; k++) w[k] = k < K ? a.w_conv[d * K + k] : 0.0f;
+    for (int k = 0; k < KR; k++) w[k] = a.w_conv[d * K + k];
     const float bias = a.b_conv ? a.b_conv[d] : 0.0f;
     float sw[KR], sb = 0.0f;
 #pragma unroll
@@ -73,7 +73,9 @@ __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
             float c = bias;
 #pragma unroll
             for (int k = 0; k < KR; k++) c = __builtin_fmaf(w[k], xv[i + KR - 1 - k], c);
-            dc[i] = gv[i] * silu_grad(c);   // 0 past the sequence end
+            // 0 past the sequence end (a select, not a product: the x
+            // repeated there may be non-finite)
+            dc[i] = t0 + i < L ? gv[i] * silu_grad(c) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < kRun; i++) {
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], dc[i + k], acc);
-            if (live && t < L) a.dx[base + t * D] = acc;
-            // dc[i] is 0 for t >= L, so these sums need no guard.
+            if (t >= L) break;   // wave-uniform: only the last run of a row is short
+            if (live) a.dx[base + t * D] = acc;
             sb += dc[i];
 #pragma unroll
             for (int k = 0; k < KR; k++) sw[k] = __builtin_fmaf(dc[i], xv[i + KR - 1 - k], sw[k]);
@@ -118,10 +120,17 @@ __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(ConvBwdArgs a) {
 hipError_t launch_conv1d_silu_bwd(const ConvBwdArgs& a, hipStream_t st) {
     const int64_t tiles = (a.D + kWave - 1) / kWave;
     const unsigned grid = static_cast<unsigned>(tiles * a.groups);
-    if (a.K == 4)
-        hipLaunchKernelGGL(conv_bwd_kernel<4>, dim3(grid), dim3(kWave), 0, st, a);
-    else
-        hipLaunchKernelGGL(conv_bwd_kernel<0>, dim3(grid), dim3(kWave), 0, st, a);
+    switch (a.K) {
+#define MSS_CONV_BWD_CASE(k)                                                        \
+    case k:                                                                         \
+        hipLaunchKernelGGL(conv_bwd_kernel<k>, dim3(grid), dim3(kWave), 0, st, a); \
+        break;
+        MSS_CONV_BWD_CASE(1) MSS_CONV_BWD_CASE(2) MSS_CONV_BWD_CASE(3) MSS_CONV_BWD_CASE(4)
+        MSS_CONV_BWD_CASE(5) MSS_CONV_BWD_CASE(6) MSS_CONV_BWD_CASE(7) MSS_CONV_BWD_CASE(8)
+#undef MSS_CONV_BWD_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(conv_bwd_reduce_kernel,

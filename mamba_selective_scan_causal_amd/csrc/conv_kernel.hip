@@ -7,7 +7,10 @@
 // HBM-bound (8 bytes per element).  Lane = channel d, so each time row is one
 // coalesced 256-byte segment per wave; each lane walks kRun consecutive steps
 // with the K-1 previous inputs in registers, and issues all of its loads
-// (the K-1 halo rows plus its kRun rows) before the first use.
+// (the K-1 halo rows plus its kRun rows) before the first use.  Each tap
+// count 1..8 is its own instantiation, so only the K real taps are summed
+// (a padded zero tap would still multiply an older input, and 0 * Inf is
+// NaN where the K-tap sum is finite).
 #include "device_math.h"
 #include "launch.h"
 
@@ -16,14 +19,13 @@ namespace {
 
 constexpr int kRun = 32;
 
-template <int KS>
+template <int K>
 __global__ __launch_bounds__(kWave) void conv_kernel(const float* __restrict__ x,
                                                      const float* __restrict__ w_conv,
                                                      const float* __restrict__ b_conv,
                                                      float* __restrict__ u, int64_t B, int64_t L,
-                                                     int64_t D, int K_rt) {
-    constexpr int KR = KS > 0 ? KS : kMaxK;
-    const int K = KS > 0 ? KS : K_rt;
+                                                     int64_t D) {
+    constexpr int KR = K;
     const int64_t tiles = (D + kWave - 1) / kWave;
     const int64_t runs = (L + kRun - 1) / kRun;
     const int64_t nblk = B * runs * tiles;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kWave) void conv_kernel(const float* __restrict__ x
 
         float w[KR];
 #pragma unroll
-        for (int k = 0; k < KR; k++) w[k] = k < K ? w_conv[d * K + k] : 0.0f;
+        for (int k = 0; k < KR; k++) w[k] = w_conv[d * K + k];
         const float bias = b_conv ? b_conv[d] : 0.0f;
 
         // v[i] = x at t0 - (KR-1) + i; zero before the start of the batch row.
@@ -76,12 +78,18 @@ __global__ __launch_bounds__(256) void state_init_kernel(const float* __restrict
 hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t st) {
     const int64_t nblk = a.B * ((a.L + kRun - 1) / kRun) * ((a.D + kWave - 1) / kWave);
     const unsigned grid = static_cast<unsigned>(nblk < (1 << 30) ? nblk : (1 << 30));
-    if (a.K == 4)
-        hipLaunchKernelGGL(conv_kernel<4>, dim3(grid), dim3(kWave), 0, st, a.x, a.w_conv,
-                           a.b_conv, a.u, a.B, a.L, a.D, a.K);
-    else
-        hipLaunchKernelGGL(conv_kernel<0>, dim3(grid), dim3(kWave), 0, st, a.x, a.w_conv,
-                           a.b_conv, a.u, a.B, a.L, a.D, a.K);
+    switch (a.K) {
+#define MSS_CONV_CASE(k)                                                                     \
+    case k:                                                                                  \
+        hipLaunchKernelGGL(conv_kernel<k>, dim3(grid), dim3(kWave), 0, st, a.x, a.w_conv,   \
+                           a.b_conv, a.u, a.B, a.L, a.D);                                    \
+        break;
+        MSS_CONV_CASE(1) MSS_CONV_CASE(2) MSS_CONV_CASE(3) MSS_CONV_CASE(4)
+        MSS_CONV_CASE(5) MSS_CONV_CASE(6) MSS_CONV_CASE(7) MSS_CONV_CASE(8)
+#undef MSS_CONV_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+constexpr int32_t kKnownFlags = MSS_FLAG_EXACT;   // every other flag bit is rejected
+
 int hip_fail(hipError_t e) {
     g_last_hip_error = static_cast<int>(e);
     return MSS_EHIP;
@@ -110,7 +112,8 @@ struct Checker {
 };
 
 int check_dims(const mss_dims* dims, bool need_l, bool need_k) {
-    if (!dims || dims->struct_size != static_cast<int32_t>(sizeof(mss_dims)) || dims->reserved != 0)
+    if (!dims || dims->struct_size != static_cast<int32_t>(sizeof(mss_dims)) ||
+        (dims->flags & ~kKnownFlags) != 0)
         return MSS_EINVAL;
     if (dims->batch < 0 || dims->d_inner < 0) return MSS_EINVAL;
     if (need_l && dims->seq_len < 0) return MSS_EINVAL;
@@ -119,33 +122,43 @@ int check_dims(const mss_dims* dims, bool need_l, bool need_k) {
     return MSS_OK;
 }
 
-// Waves per CU for the scan (2 per SIMD) and the shortest segment; both can
-// be overridden through the environment for tuning experiments.
-int64_t env_or(const char* name, int64_t dflt) {
-    const char* v = std::getenv(name);
-    if (!v || !*v) return dflt;
-    const long long x = std::atoll(v);
-    return x > 0 ? x : dflt;
-}
+// The time split.  Segment lengths depend on the problem shape alone (never
+// on the device or the environment), so a call's output bits are a function
+// of its inputs and shape.  The constants can be overridden at build time
+// (-D...) for tuning experiments.
+#ifndef MSS_SCAN_TARGET_WAVES
+#define MSS_SCAN_TARGET_WAVES 2048   // two waves on each SIMD of a 256-CU MI355X
+#endif
+#ifndef MSS_SCAN_MIN_SEG
+#define MSS_SCAN_MIN_SEG 64
+#endif
+#ifndef MSS_BWD_TARGET_WAVES
+#define MSS_BWD_TARGET_WAVES 2048
+#endif
+#ifndef MSS_BWD_MIN_SEG
+#define MSS_BWD_MIN_SEG 64
+#endif
+#ifndef MSS_SSD_TARGET_WG
+#define MSS_SSD_TARGET_WG 1280       // about five 4-wave workgroups per CU
+#endif
+#ifndef MSS_SSD_MIN_SEG
+#define MSS_SSD_MIN_SEG 64
+#endif
 
-int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev < 0 || dev >= 64) return 256;
-    int c = cache[dev].load(std::memory_order_relaxed);
-    if (c == 0) {
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-            c = 256;
-        cache[dev].store(c, std::memory_order_relaxed);
-    }
-    return c;
+bool exact(const mss_dims* dims) { return (dims->flags & MSS_FLAG_EXACT) != 0; }
+
+// Segment length (steps of the flattened (tile, t) space) for `total` steps
+// over tiles of L steps: equal segments for about `target` waves, none
+// shorter than `min_seg`; MSS_FLAG_EXACT: one segment per tile.
+int64_t split(int64_t total, int64_t L, int64_t target, int64_t min_seg, bool whole_tiles) {
+    if (whole_tiles) return L > 0 ? L : 1;
+    int64_t seg = (total + target - 1) / target;
+    if (seg < min_seg) seg = min_seg;
+    return seg < 1 ? 1 : seg;
 }
 
 mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const float* B,
                           const float* C, const float* z) {
-    static const int64_t waves_per_cu = env_or("MSS_SCAN_WAVES_PER_CU", 8);
-    static const int64_t min_seg = env_or("MSS_SCAN_MIN_SEG", 64);
     mss::ScanShape s;
     s.B = dims->batch;
     s.L = dims->seq_len;
@@ -154,10 +167,7 @@ mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const flo
     s.K = static_cast<int>(dims->d_conv);
     s.tiles_per_b = (s.D + 63) / 64;
     s.total = s.B * s.tiles_per_b * s.L;
-    const int64_t target = cu_count() * waves_per_cu;
-    int64_t seg = (s.total + target - 1) / target;
-    if (seg < min_seg) seg = min_seg;
-    s.seg = seg;
+    s.seg = split(s.total, s.L, MSS_SCAN_TARGET_WAVES, MSS_SCAN_MIN_SEG, exact(dims));
     s.ld_src = ld.x;
     s.ld_z = ld.z;
     s.ld_delta = ld.delta;
@@ -251,11 +261,9 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // Work split of the scan backward: the flattened (channel tile, t) space cut
 // into segments of equal length, about two waves per SIMD, but no segment
-// shorter than MSS_BWD_MIN_SEG steps (default 64): below that the two decay
-// replays of a segment outweigh its own steps.
+// shorter than 64 steps: below that the two decay replays of a segment
+// outweigh its own steps.
 mss::BwdShape bwd_shape(const mss_dims* dims) {
-    static const int64_t waves_per_cu = env_or("MSS_BWD_WAVES_PER_CU", 8);
-    static const int64_t min_seg = env_or("MSS_BWD_MIN_SEG", 64);
     mss::BwdShape s;
     s.B = dims->batch;
     s.L = dims->seq_len;
@@ -263,10 +271,7 @@ mss::BwdShape bwd_shape(const mss_dims* dims) {
     s.N = static_cast<int>(dims->d_state);
     s.tiles_per_b = (s.D + kBwdTile - 1) / kBwdTile;
     s.total = s.B * s.tiles_per_b * s.L;   // fits: B L D was counted without overflow
-    const int64_t target = cu_count() * waves_per_cu;
-    int64_t seg = (s.total + target - 1) / target;
-    if (seg < min_seg) seg = min_seg;
-    if (seg < 1) seg = 1;
+    const int64_t seg = split(s.total, s.L, MSS_BWD_TARGET_WAVES, MSS_BWD_MIN_SEG, exact(dims));
     s.seg = seg;
     s.waves = (s.total + seg - 1) / seg;
     s.blocks_per_seg = (seg + kBwdBlock - 1) / kBwdBlock;
@@ -300,7 +305,7 @@ bool bwd_layout(const mss::BwdShape& s, BwdLayout& o) {
 int64_t conv_bwd_groups(const mss_dims* dims) {
     const int64_t tiles = (dims->d_inner + 63) / 64;
     const int64_t jobs = dims->batch * ((dims->seq_len + kConvRun - 1) / kConvRun);
-    const int64_t target = cu_count() * 8;
+    const int64_t target = MSS_BWD_TARGET_WAVES;   // fixed: the dw, db summation order depends on it
     int64_t g = tiles > 0 ? (target + tiles - 1) / tiles : 1;
     if (g > jobs) g = jobs;
     if (g < 1) g = 1;
@@ -325,9 +330,65 @@ int zero_fill(float* p, int64_t n, hipStream_t stream) {
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
+bool ssd_dims_ok(const mss_ssd_dims* dims) {
+    return dims && dims->struct_size == static_cast<int32_t>(sizeof(mss_ssd_dims)) &&
+           (dims->flags & ~kKnownFlags) == 0;
+}
+
+// SSD segments per (batch row, head): about MSS_SSD_TARGET_WG workgroups in
+// all (two are resident per CU at a time; the surplus evens out the finish),
+// none shorter than MSS_SSD_MIN_SEG steps (two chunks), so that the replay
+// that rebuilds a segment's initial state does not outweigh its own steps;
+// then rounded so that every segment has the same number of chunks.
+int64_t ssd_segments(int64_t bh, int64_t nchunks, bool whole) {
+    if (whole || bh <= 0 || nchunks <= 0) return 1;
+    const int64_t Q = mss::ssd_chunk_len();
+    int64_t nseg = MSS_SSD_TARGET_WG / bh;
+    const int64_t min_chunks = (MSS_SSD_MIN_SEG + Q - 1) / Q;
+    const int64_t max_seg = (nchunks + min_chunks - 1) / min_chunks;
+    if (nseg > max_seg) nseg = max_seg;
+    if (nseg < 1) nseg = 1;
+    const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
+    return (nchunks + seg_chunks - 1) / seg_chunks;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mss_time_split(const mss_dims* dims, int op, int64_t* segment_steps) {
+    if (!segment_steps) return MSS_EINVAL;
+    *segment_steps = 0;
+    const int st = check_dims(dims, true, false);
+    if (st != MSS_OK) return st;
+    int64_t MD;
+    if (!count(MD, {dims->batch, dims->seq_len, dims->d_inner})) return MSS_EINVAL;
+    if (op == MSS_OP_SELECTIVE_SCAN) {
+        const mss_strides ld = dense_strides(dims);
+        *segment_steps = MD > 0 ? scan_shape(dims, ld, nullptr, nullptr, nullptr).seg : 0;
+        return MSS_OK;
+    }
+    if (op == MSS_OP_SELECTIVE_SCAN_BACKWARD) {
+        *segment_steps = MD > 0 ? bwd_shape(dims).seg : 0;
+        return MSS_OK;
+    }
+    return MSS_EINVAL;
+}
+
+int mss_ssd_time_split(const mss_ssd_dims* dims, int64_t* segment_steps) {
+    if (!segment_steps) return MSS_EINVAL;
+    *segment_steps = 0;
+    if (!ssd_dims_ok(dims) || dims->batch < 0 || dims->seq_len < 0 || dims->n_heads < 1)
+        return MSS_EINVAL;
+    int64_t bh;
+    if (!count(bh, {dims->batch, dims->n_heads})) return MSS_EINVAL;
+    if (bh == 0 || dims->seq_len == 0) return MSS_OK;
+    const int64_t Q = mss::ssd_chunk_len();
+    const int64_t nchunks = (dims->seq_len + Q - 1) / Q;
+    const int64_t nseg = ssd_segments(bh, nchunks, (dims->flags & MSS_FLAG_EXACT) != 0);
+    *segment_steps = (nchunks + nseg - 1) / nseg * Q;
+    return MSS_OK;
+}
 
 int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes) {
     if (!bytes) return MSS_EINVAL;
@@ -551,9 +612,7 @@ int mss_selective_step(const mss_dims* dims, int disc, const float* x, const flo
 int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float* dt, const float* A_log,
                  const float* B, const float* C, const float* D_vec, const float* dt_bias,
                  const float* h0, float* y, float* h_last, hipStream_t stream) {
-    if (!dims || dims->struct_size != static_cast<int32_t>(sizeof(mss_ssd_dims)) ||
-        dims->reserved != 0)
-        return MSS_EINVAL;
+    if (!ssd_dims_ok(dims)) return MSS_EINVAL;
     const int64_t Bt = dims->batch, L = dims->seq_len, H = dims->n_heads, P = dims->head_dim;
     const int64_t N = dims->d_state, G = dims->n_groups;
     if (Bt < 0 || L < 0 || H < 1 || G < 1 || H % G != 0 || !mss::ssd_supported(P, N))
@@ -582,22 +641,11 @@ int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float
         const hipError_t e = mss::launch_state_init(h0, h_last, BHPN, stream);
         return e == hipSuccess ? MSS_OK : hip_fail(e);
     }
-    // Segments: about five workgroups per CU (two are resident at a time;
-    // the surplus evens out the finish), none shorter than MSS_SSD_MIN_SEG
-    // steps (default 64, two chunks), so that the replay that rebuilds a
-    // segment's initial state does not outweigh its own steps.
-    static const int64_t wg_per_cu = env_or("MSS_SSD_WG_PER_CU", 5);
-    static const int64_t min_seg = env_or("MSS_SSD_MIN_SEG", 64);
     const int64_t Q = mss::ssd_chunk_len();
     const int64_t nchunks = (L + Q - 1) / Q;
+    const int64_t nseg = ssd_segments(Bt * H, nchunks, (dims->flags & MSS_FLAG_EXACT) != 0);
     const int64_t bh = Bt * H;
-    int64_t nseg = (cu_count() * wg_per_cu) / bh;
-    const int64_t min_chunks = (min_seg + Q - 1) / Q;
-    const int64_t max_seg = (nchunks + min_chunks - 1) / min_chunks;
-    if (nseg > max_seg) nseg = max_seg;
-    if (nseg < 1) nseg = 1;
     const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
-    nseg = (nchunks + seg_chunks - 1) / seg_chunks;
     if (bh * nseg > INT32_MAX) return MSS_EINVAL;
     const mss::SsdArgs a{disc, Bt, L, H, P, N, G, nseg, seg_chunks, x, dt, A_log, B, C,
                          D_vec, dt_bias, h0, y, h_last};

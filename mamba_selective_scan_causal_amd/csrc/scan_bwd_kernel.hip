@@ -26,7 +26,8 @@
 //      checkpoint workspace (2 KB per block).
 //   3. The adjoint carried into t1-1 by decay-bounded reverse replay: walk
 //      delta forward from t1 until every lane's slowest state has decayed by
-//      2^-24, then run the adjoint recurrence backwards from there with g = 0.
+//      2^-c (c = MSS_REPLAY_DECAY_BITS), then run the adjoint recurrence
+//      backwards from there with g = 0.
 //   4. Blocks in reverse order: reload the block's checkpoint, recompute its
 //      8 states into registers (emitting dz and the dC terms on the way),
 //      then run the adjoint through the block (emitting du, ddelta and the dB
@@ -46,7 +47,7 @@ namespace {
 constexpr int kT = 8;                          // steps per block
 constexpr int kH = 8;                          // states per lane
 constexpr int kBackBlk = 16;
-constexpr float kDecayCut = 24.0f;
+constexpr float kDecayCut = MSS_REPLAY_DECAY_BITS;
 constexpr float kSmallX = 0.015625f;           // expm1 cubic below |dv A| = 2^-6
 constexpr float kSmallX2 = kSmallX * kLog2e;
 constexpr int kNone = 0, kFirst = 1, kAll = 2;  // which states take the accurate path

@@ -25,14 +25,16 @@
 // h(t0 - 1).  Because the recurrence forgets exponentially -- the part of
 // h(t0-1) that comes from before step s is multiplied by
 // prod_{r=s}^{t0-1} aBar_r = exp(A_n * sum_r dv_r) -- the wave first walks
-// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= 24 ln 2 holds in
-// every lane (or t = 0 is reached), then replays the recurrence forward from
-// that step with h = 0 (state only, no outputs).  What this drops is exactly
-// the state at the replay start times a factor <= 2^-24 per state (the unit
-// roundoff of fp32: below one rounding of the state it came from); reaching
-// t = 0 makes it exact.  States that decay faster than the slowest one join
-// the replay later, each once its own decay to t0 reaches the same bound.
-// No workspace and no inter-wave synchronisation.
+// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= c ln 2 holds in
+// every lane (c = MSS_REPLAY_DECAY_BITS, or t = 0 is reached), then replays
+// the recurrence forward from that step with h = 0 (state only, no
+// outputs).  What this drops is exactly the state at the replay start times
+// a factor <= 2^-c per state -- small against the outputs unless that state
+// is ~2^c / 10^4 times larger than they are; reaching t = 0 makes it exact.
+// States that decay faster than the slowest one join the replay later, each
+// once its own decay to t0 reaches the same bound.  MSS_FLAG_EXACT makes
+// every segment a whole tile (no replay).  No workspace and no inter-wave
+// synchronisation.
 #include "device_math.h"
 #include "launch.h"
 
@@ -41,7 +43,7 @@ namespace {
 
 constexpr int kT = 8;                         // steps per straight-line block
 constexpr int kBackBlk = 16;                  // delta loads in flight in the backward walk
-constexpr float kDecayCut = 24.0f;            // replay until the carried part decays by 2^-24
+constexpr float kDecayCut = MSS_REPLAY_DECAY_BITS;   // replay until the carried part has decayed this many bits
 // Below |dv*A| = 2^-6 the decay is applied through expm1 (see step()).
 constexpr float kSmallX = 0.015625f;
 constexpr float kSmallX2 = kSmallX * kLog2e;  // the same bound in log2 units
@@ -422,7 +424,7 @@ struct Scan {
     // Replay of steps [tb, te), state only; S = the lane's sum of dv over
     // [tb, te).  The replay start was chosen for the slowest state; a faster
     // state n joins only at the last block start from which its own decay
-    // to te, 2^(-|A2_n| sum dv), is still <= 2^-24 in every lane, and is 0
+    // to te, 2^(-|A2_n| sum dv), is still <= 2^-c in every lane, and is 0
     // until then.  That drops no more than the replay start itself drops, at
     // a fraction of the cost when the decay rates differ (|A| = 1..16 makes
     // the replay ~4x cheaper).  A replay from t = 0 is exact: every state

@@ -28,8 +28,9 @@
 // three waves form the three nonzero 16 x 16 tiles of L o C B^T; each wave
 // then forms its y columns and updates its S columns.  A segment that starts
 // at t0 > 0 first rebuilds S(t0 - 1) by replaying the state update from the
-// point where every contribution before it has decayed by 2^-24 (for a
-// scalar-decay head this walk is exact and uniform), as the Mamba-1 kernels do.
+// point where every contribution before it has decayed by 2^-c, with
+// c = MSS_REPLAY_DECAY_BITS (for a scalar-decay head the walk is uniform
+// across the head's channels), as the Mamba-1 kernels do.
 #include "device_math.h"
 #include "launch_ssd.h"
 
@@ -39,7 +40,7 @@ namespace {
 constexpr int kQ = 32;            // steps per chunk
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr float kCut = 24.0f;     // replay until the carried part decays by 2^-24
+constexpr float kCut = MSS_REPLAY_DECAY_BITS;   // replay until the carried part has decayed this many bits
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -334,8 +335,8 @@ struct Ssd {
     }
 
     // First step of the replay that rebuilds S(t0 - 1): walk dt backwards
-    // until sum dv |A| >= 24 ln 2 (every contribution before it has decayed
-    // by 2^-24), or t = 0.  One wave walks 64 steps at a time.
+    // until sum dv |A| >= c ln 2 (every contribution before it has decayed
+    // by 2^-c), or t = 0.  One wave walks 64 steps at a time.
     __device__ __forceinline__ int64_t replay_start(int64_t t0) const {
         if (t0 == 0) return 0;
         int64_t* res = reinterpret_cast<int64_t*>(lds + C_::oMisc);

@@ -35,7 +35,7 @@ float* misaligned(int i) { return reinterpret_cast<float*>(reinterpret_cast<char
 mss_dims dims(int64_t b, int64_t l, int64_t d, int64_t n, int64_t k) {
     mss_dims x;
     x.struct_size = sizeof(mss_dims);
-    x.reserved = 0;
+    x.flags = 0;
     x.batch = b;
     x.seq_len = l;
     x.d_inner = d;
@@ -47,7 +47,7 @@ mss_dims dims(int64_t b, int64_t l, int64_t d, int64_t n, int64_t k) {
 mss_ssd_dims ssd_dims(int64_t b, int64_t l, int64_t h, int64_t p, int64_t n, int64_t g) {
     mss_ssd_dims x;
     x.struct_size = sizeof(mss_ssd_dims);
-    x.reserved = 0;
+    x.flags = 0;
     x.batch = b;
     x.seq_len = l;
     x.n_heads = h;
@@ -104,8 +104,8 @@ int main() {
     bad.struct_size = 8;
     expect(scan(&bad, 0, fake(1), fake(9)), MSS_EINVAL, "scan: struct_size");
     bad = d;
-    bad.reserved = 1;
-    expect(scan(&bad, 0, fake(1), fake(9)), MSS_EINVAL, "scan: reserved");
+    bad.flags = 2;
+    expect(scan(&bad, 0, fake(1), fake(9)), MSS_EINVAL, "scan: unknown flag");
     mss_dims n17 = dims(2, 64, 128, 17, 4);
     expect(scan(&n17, 0, fake(1), fake(9)), MSS_EINVAL, "scan: N = 17");
     expect(scan(&d, 7, fake(1), fake(9)), MSS_EINVAL, "scan: disc");

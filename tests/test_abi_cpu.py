@@ -70,7 +70,9 @@ def test_scan_validation(L):
     bad.struct_size = 40
     assert scan_call(L, bad) == EINVAL
     bad = mss.make_dims(2, 16, 64, 16, 4)
-    bad.reserved = 1
+    bad.flags = 2                                                         # unknown flag bit
+    assert scan_call(L, bad) == EINVAL
+    bad.flags = -1
     assert scan_call(L, bad) == EINVAL
     assert scan_call(L, mss.make_dims(2, 16, 64, 17, 4)) == EINVAL       # N > 16
     assert scan_call(L, mss.make_dims(2, 16, 64, 0, 4)) == EINVAL        # N < 1
@@ -309,3 +311,19 @@ def test_ssd_validation(L):
     assert ssd_call(L, d, x=ctypes.c_void_p(BASE + (1 << 32) + 8)) == EALIGN
     assert ssd_call(L, mss.make_ssd_dims(0, 64, 8, 64, 128, 2)) == 0        # empty: nothing to do
     assert ctypes.sizeof(mss.SsdDims) == 56
+
+
+def test_binding_loads_libmss_on_torchs_hip_runtime():
+    """libmss must resolve libamdhip64.so.7 to the runtime torch loaded: a
+    fresh process that asks the binding for the library (before importing
+    torch itself) ends up with one HIP runtime mapped, torch's."""
+    import subprocess
+    import sys
+    code = ("import mamba_selective_scan_causal_amd as m; m.lib(); "
+            "maps = [l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l]; "
+            "print(sorted(set(maps)))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))), timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1 and "torch" in libs[0], libs

@@ -173,3 +173,37 @@ def test_ssd_contains_nonfinite_inputs():
     assert not np.isfinite(oy[w.seq_len + 650:, :]).all()
     assert_close(host(y), oy, "y")
     assert_close(host(hl), ohl, "h_last")
+
+
+@pytest.mark.parametrize("K", (3, 8))
+def test_conv_contains_nonfinite_inputs(K):
+    """+Inf and NaN in x with d_conv = 3 and 8, forward and backward of the
+    conv1d + SiLU on their own: only the K taps of the method may meet a
+    poisoned input, so outputs K or more steps after it (forward) or before
+    it (dx) stay finite and match the oracle.  +Inf also sits at the last
+    step of row 1, where a window running past the sequence end would meet
+    it again."""
+    import torch
+    w = gen.SMALL.with_(name=f"nonfinite_conv_k{K}", batch=2, seq_len=300, d_inner=100,
+                        d_conv=K, b_conv="normal")
+    inp = gen.generate(w)
+    L = w.seq_len
+    inp["x"][0 * L + 100, 7] = np.inf
+    inp["x"][0 * L + 200, 70] = np.nan
+    inp["x"][1 * L + L - 1, 30] = np.inf
+    d = {k: dev(v) for k, v in inp.items()}
+    u = mss.conv1d_silu(d["x"], d["w_conv"], d["b_conv"], batch=w.batch, seq_len=L)
+    torch.cuda.synchronize()
+    ou = oracle.conv1d_silu(inp["x"], inp["w_conv"], inp["b_conv"], batch=w.batch, seq_len=L)
+    assert np.isfinite(ou[100 + K:L, 7]).all() and np.isfinite(ou[200 + K:L, 70]).all()
+    assert_close(host(u), ou, "u")
+    du = gen.cotangent(w)
+    gx, gw, gb = mss.conv1d_silu_backward(d["x"], d["w_conv"], d["b_conv"], dev(du),
+                                          batch=w.batch, seq_len=L)
+    torch.cuda.synchronize()
+    ox, ow, ob = oracle.conv1d_silu_backward(inp["x"], inp["w_conv"], inp["b_conv"], du,
+                                             batch=w.batch, seq_len=L)
+    assert np.isfinite(ox[:100 - K, 7]).all() and np.isfinite(ox[L:2 * L - K, 30]).all()
+    assert np.isfinite(ox).sum() > 0.99 * ox.size
+    for name, got, want in (("dx", gx, ox), ("dw", gw, ow), ("db", gb, ob)):
+        assert_close(host(got), want, name)

@@ -421,3 +421,38 @@ def test_strided_column_slices(entry, R, disc):
     assert_close(host(hl), ohl, "h_last")
     outside = torch.cat([YB[:, :3], YB[:, 3 + D:]], dim=1)
     assert torch.isnan(outside).all().item(), "wrote outside the y slice"
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_time_split_changes_agree(disc):
+    """The segment length follows the shape: batch row 3 of the 8 x 2048 x 1536
+    workload run inside the batch (192-step segments), alone (64-step
+    segments) and with MSS_FLAG_EXACT (no split) gives three different sets
+    of replay cuts; all three match the oracle and each other within 1e-4."""
+    import torch
+    w = gen.MAMBA_130M
+    inp = gen.generate(w)
+    L, D = w.seq_len, w.d_inner
+    seg_all = mss.time_split(mss.OP_SELECTIVE_SCAN, batch=w.batch, seq_len=L, d_inner=D,
+                             d_state=w.d_state, d_conv=w.d_conv)
+    seg_one = mss.time_split(mss.OP_SELECTIVE_SCAN, batch=1, seq_len=L, d_inner=D,
+                             d_state=w.d_state, d_conv=w.d_conv)
+    seg_exact = mss.time_split(mss.OP_SELECTIVE_SCAN, batch=1, seq_len=L, d_inner=D,
+                               d_state=w.d_state, d_conv=w.d_conv, exact=True)
+    assert (seg_all, seg_one, seg_exact) == (192, 64, L)
+    y_all, _, _ = run_core(inp, w, disc)
+    rows = slice(3 * L, 4 * L)
+    one = {k: (np.ascontiguousarray(v[rows]) if v.shape[0] == w.M else v) for k, v in inp.items()}
+    w1 = w.with_(batch=1)
+    y_one, _, _ = run_core(one, w1, disc)
+    d = {k: dev(v) for k, v in one.items()}
+    y_ex = nan_like((L, D))
+    mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"], d["B"], d["C"],
+                    d["D_vec"], d["z"], None, batch=1, seq_len=L, disc=disc, out=y_ex, exact=True)
+    torch.cuda.synchronize()
+    y_ex = host(y_ex)
+    oy, _, _ = oracle_core(one, w1, disc)
+    for name, got in (("in the batch", y_all[rows]), ("alone", y_one), ("exact", y_ex)):
+        assert_close(got, oy, f"y {name}")
+    assert_close(y_all[rows], y_ex, "batched vs exact")
+    assert_close(y_one, y_ex, "alone vs exact")
