@@ -19,8 +19,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers to dense, row-major fp32 arrays
  *     on the current HIP device, allocated and owned by the caller.  The
- *     library allocates nothing, keeps no device state and never frees a
- *     caller buffer; the backward passes take a caller workspace.
+ *     library allocates nothing and never frees a caller buffer; the backward
+ *     passes take a caller workspace.  Its only device state is the static
+ *     scratch array of mss_selective_scan_backward_noalloc.
  *   - Every pointer must be 16-byte aligned (MSS_EALIGN otherwise), except
  *     the activation and B/C tensors of the *_strided entry points (4 bytes).
  *   - Outputs may not overlap any input (MSS_EALIAS), except the state
@@ -56,6 +57,7 @@ extern "C" {
 #define MSS_EALIAS (-3)     /* an output overlaps an input */
 #define MSS_EWORKSPACE (-4) /* workspace NULL or smaller than mss_workspace_bytes */
 #define MSS_EHIP (-5)       /* a HIP runtime call or kernel launch failed; see mss_last_hip_error */
+#define MSS_ESCRATCH (-6)   /* needs more than MSS_NOALLOC_SCRATCH_BYTES (the *_noalloc entry point) */
 
 /* Problem sizes.  `struct_size` must be sizeof(mss_dims): it guards against a
  * caller built against a different layout of this struct.
@@ -236,6 +238,33 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
                                 float* dh0, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc:
+ * mss_selective_scan_backward with the workspace taken from a static device
+ * array inside the library instead of from the caller.  Same arguments and
+ * results (the same kernels), minus the workspace.
+ *   - The array holds MSS_NOALLOC_SCRATCH_BYTES (256 MiB) on every GPU the
+ *     library runs on, from the time its code is loaded until the process
+ *     ends.  A problem whose mss_workspace_bytes(MSS_OP_SELECTIVE_SCAN_BACKWARD)
+ *     exceeds it is refused with MSS_ESCRATCH before anything is launched
+ *     (B2 L512 D256 needs 3.3 MiB, B4 L2048 D1024 101 MiB, B8 L2048 D1536
+ *     294 MiB: refused).
+ *   - The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ *     library routine.  Its first call on a device looks up the array's
+ *     device address (hipGetSymbolAddress, with that device current).
+ *   - All calls on one GPU share the one array, which keeps the last call's
+ *     contents (nothing in it needs to start at zero).  Calls that overlap
+ *     in time on one GPU -- on two streams, or from two threads -- race on
+ *     it: order them on one stream or use the workspace entry point.      */
+#define MSS_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int mss_selective_scan_backward_noalloc(const mss_dims* dims, int disc, const float* u,
+                                        const float* delta, const float* A_log, const float* B,
+                                        const float* C, const float* D_vec, const float* z,
+                                        const float* h0, const float* dout, float* du,
+                                        float* ddelta, float* dA_log, float* dB, float* dC,
+                                        float* dD_vec, float* dz, float* dh0,
+                                        hipStream_t stream);
 
 /* Gradients of u = SiLU(conv1d(x)) (mss_conv1d_silu) against du (M, D), the
  * total gradient reaching u:  dc = du * SiLU'(c),

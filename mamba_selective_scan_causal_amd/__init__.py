@@ -78,11 +78,14 @@ EXPORTS = ("mss_conv1d_silu", "mss_selective_scan", "mss_mamba1_core", "mss_sele
            "mss_selective_scan_strided", "mss_mamba1_core_strided",
            "mss_workspace_bytes", "mss_selective_scan_backward", "mss_conv1d_silu_backward",
            "mss_ssd_scan", "mss_time_split", "mss_ssd_time_split",
+           "mss_selective_scan_backward_noalloc",
            "mss_strerror", "mss_version", "mss_last_hip_error")
 
 OP_SELECTIVE_SCAN_BACKWARD = 1
 OP_CONV1D_SILU_BACKWARD = 2
 OP_SELECTIVE_SCAN = 3
+NOALLOC_SCRATCH_BYTES = 256 << 20     # MSS_NOALLOC_SCRATCH_BYTES
+MSS_ESCRATCH = -6
 
 _lib = None
 
@@ -112,6 +115,7 @@ def lib():
         sz = ctypes.c_size_t
         L.mss_workspace_bytes.argtypes = [dp, i, ctypes.POINTER(sz)]
         L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
+        L.mss_selective_scan_backward_noalloc.argtypes = [dp, i] + [p] * 17
         L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
         L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims), i] + [p] * 11
         L.mss_time_split.argtypes = [dp, i, ctypes.POINTER(ctypes.c_int64)]
@@ -120,7 +124,7 @@ def lib():
                   "mss_selective_step", "mss_selective_scan_strided", "mss_mamba1_core_strided",
                   "mss_workspace_bytes", "mss_selective_scan_backward",
                   "mss_conv1d_silu_backward", "mss_ssd_scan", "mss_time_split",
-                  "mss_ssd_time_split", "mss_version",
+                  "mss_ssd_time_split", "mss_selective_scan_backward_noalloc", "mss_version",
                   "mss_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         L.mss_strerror.argtypes = [ctypes.c_int]
@@ -402,6 +406,36 @@ def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
         _ptr(g["dC"], "dC", (M, N)), _ptr(g["dD"], "dD", (D,), False),
         _ptr(g["dz"], "dz", (M, D), False), _ptr(g["dh0"], "dh0", (batch, D, N), False),
         wp, wn, _stream(stream)))
+    return g
+
+
+def selective_scan_backward_noalloc(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
+                                    seq_len, disc, need_dh0=False, out=None, stream=None,
+                                    exact=False):
+    """``selective_scan_backward`` through the entry point whose workspace is the
+    library's static scratch array (for callers that cannot allocate; at most
+    NOALLOC_SCRATCH_BYTES of workspace; calls overlapping on one GPU race).
+    ``out``: optional dict of preallocated gradient tensors (the keys of the
+    result), so that the call itself allocates nothing."""
+    D, N = A_log.shape
+    M = batch * seq_len
+    shapes = {"du": (M, D), "ddelta": (M, D), "dA_log": (D, N), "dB": (M, N), "dC": (M, N),
+              "dD": (D,), "dz": (M, D), "dh0": (batch, D, N)}
+    want = {"du": True, "ddelta": True, "dA_log": True, "dB": True, "dC": True,
+            "dD": D_vec is not None, "dz": z is not None, "dh0": need_dh0}
+    out = dict(out or {})
+    g = {k: (out[k] if k in out else _empty(shapes[k], u)) if want[k] else None for k in shapes}
+    dims = make_dims(batch, seq_len, D, N, 1, exact)
+    _check("mss_selective_scan_backward_noalloc", lib().mss_selective_scan_backward_noalloc(
+        ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
+        _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
+        _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
+        _ptr(h0, "h0", (batch, D, N), False), _ptr(dout, "dout", (M, D)),
+        _ptr(g["du"], "du", (M, D)), _ptr(g["ddelta"], "ddelta", (M, D)),
+        _ptr(g["dA_log"], "dA_log", (D, N)), _ptr(g["dB"], "dB", (M, N)),
+        _ptr(g["dC"], "dC", (M, N)), _ptr(g["dD"], "dD", (D,), False),
+        _ptr(g["dz"], "dz", (M, D), False), _ptr(g["dh0"], "dh0", (batch, D, N), False),
+        _stream(stream)))
     return g
 
 

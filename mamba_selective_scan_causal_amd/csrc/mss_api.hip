@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -354,6 +355,127 @@ int64_t ssd_segments(int64_t bh, int64_t nchunks, bool whole) {
 
 }  // namespace
 
+// ---- the static scratch array of mss_selective_scan_backward_noalloc -------
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the scan backward's workspace in a
+// device array of the library itself.  Each GPU the library runs on holds
+// its own copy from the time the code object is loaded until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is taken once per device, with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = static_cast<size_t>(MSS_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return MSS_EINVAL;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e);
+            if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0) return MSS_EHIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MSS_OK;
+}
+
+// The scan backward with its workspace from the caller (use_scratch false) or
+// from the library's static scratch array (use_scratch true; workspace is
+// then ignored).
+int scan_bwd_common(const mss_dims* dims, int disc, const float* u, const float* delta,
+                    const float* A_log, const float* B, const float* C, const float* D_vec,
+                    const float* z, const float* h0, const float* dout, float* du,
+                    float* ddelta, float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
+                    float* dh0, bool use_scratch, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    int st = check_dims(dims, true, false);
+    if (st != MSS_OK) return st;
+    if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
+    const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
+    int64_t MD, MN, DN, BDN;
+    if (!count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) || !count(DN, {D, N}) ||
+        !count(BDN, {Bt, D, N}))
+        return MSS_EINVAL;
+    if (z && !dz && MD > 0) return MSS_EINVAL;
+    Checker ck;
+    ck.in(u, MD, true);
+    ck.in(delta, MD, true);
+    ck.in(A_log, DN, true);
+    ck.in(B, MN, true);
+    ck.in(C, MN, true);
+    ck.in(D_vec, D, false);
+    ck.in(z, MD, false);
+    ck.in(h0, BDN, false);
+    ck.in(dout, MD, true);
+    ck.out(du, MD, true);
+    ck.out(ddelta, MD, true);
+    ck.out(dA_log, DN, true);
+    ck.out(dB, MN, true);
+    ck.out(dC, MN, true);
+    ck.out(dD_vec, D, false);
+    ck.out(dz, z ? MD : 0, false);
+    ck.out(dh0, BDN, false);
+    int64_t need = 0;
+    mss::BwdShape s{};
+    BwdLayout lay{};
+    if (MD > 0) {
+        s = bwd_shape(dims);
+        if (!bwd_layout(s, lay)) return MSS_EINVAL;
+        if (s.waves > INT32_MAX) return MSS_EINVAL;   // grid size
+        need = lay.total;
+    }
+    // The workspace is an output like the others: it may not overlap anything.
+    if (!use_scratch && need > 0 && workspace) ck.outs.push_back({workspace, need});
+    st = ck.finish();
+    if (st != MSS_OK) return st;
+    if (use_scratch) {
+        // checked before any HIP call: a request past the static array's size
+        // is refused without touching the device
+        if (need > static_cast<int64_t>(kScratchBytes)) return MSS_ESCRATCH;
+        if (need > 0) {
+            st = scratch_address(&workspace);
+            if (st != MSS_OK) return st;
+            workspace_bytes = kScratchBytes;
+        }
+    } else {
+        st = check_workspace(workspace, workspace_bytes, need);
+        if (st != MSS_OK) return st;
+    }
+    if (MD == 0) {
+        // Nothing depends on the parameters: their gradients are zero.
+        if ((st = zero_fill(dA_log, DN, stream)) != MSS_OK) return st;
+        if ((st = zero_fill(dD_vec, D, stream)) != MSS_OK) return st;
+        return zero_fill(dh0, BDN, stream);
+    }
+    s.bc_vec = N == 16 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
+               reinterpret_cast<uintptr_t>(C) % 16 == 0;
+    char* w = static_cast<char*>(workspace);
+    const mss::BwdArgs a{disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta, dA_log,
+                         dB, dC, dD_vec, z ? dz : nullptr, dh0,
+                         reinterpret_cast<float*>(w + lay.ckpt),
+                         reinterpret_cast<float*>(w + lay.partB),
+                         reinterpret_cast<float*>(w + lay.partC),
+                         reinterpret_cast<float*>(w + lay.partA),
+                         reinterpret_cast<float*>(w + lay.partD)};
+    const hipError_t e = mss::launch_scan_bwd(a, s, stream);
+    return e == hipSuccess ? MSS_OK : hip_fail(e);
+}
+
+}  // namespace
+
 extern "C" {
 
 int mss_time_split(const mss_dims* dims, int op, int64_t* segment_steps) {
@@ -423,66 +545,20 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
                                 float* dh0, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-    int st = check_dims(dims, true, false);
-    if (st != MSS_OK) return st;
-    if (disc != MSS_DISC_ZOH && disc != MSS_DISC_EULER) return MSS_EINVAL;
-    const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
-    int64_t MD, MN, DN, BDN;
-    if (!count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) || !count(DN, {D, N}) ||
-        !count(BDN, {Bt, D, N}))
-        return MSS_EINVAL;
-    if (z && !dz && MD > 0) return MSS_EINVAL;
-    Checker ck;
-    ck.in(u, MD, true);
-    ck.in(delta, MD, true);
-    ck.in(A_log, DN, true);
-    ck.in(B, MN, true);
-    ck.in(C, MN, true);
-    ck.in(D_vec, D, false);
-    ck.in(z, MD, false);
-    ck.in(h0, BDN, false);
-    ck.in(dout, MD, true);
-    ck.out(du, MD, true);
-    ck.out(ddelta, MD, true);
-    ck.out(dA_log, DN, true);
-    ck.out(dB, MN, true);
-    ck.out(dC, MN, true);
-    ck.out(dD_vec, D, false);
-    ck.out(dz, z ? MD : 0, false);
-    ck.out(dh0, BDN, false);
-    int64_t need = 0;
-    mss::BwdShape s{};
-    BwdLayout lay{};
-    if (MD > 0) {
-        s = bwd_shape(dims);
-        if (!bwd_layout(s, lay)) return MSS_EINVAL;
-        if (s.waves > INT32_MAX) return MSS_EINVAL;   // grid size
-        need = lay.total;
-    }
-    // The workspace is an output like the others: it may not overlap anything.
-    if (need > 0 && workspace) ck.outs.push_back({workspace, need});
-    st = ck.finish();
-    if (st != MSS_OK) return st;
-    st = check_workspace(workspace, workspace_bytes, need);
-    if (st != MSS_OK) return st;
-    if (MD == 0) {
-        // Nothing depends on the parameters: their gradients are zero.
-        if ((st = zero_fill(dA_log, DN, stream)) != MSS_OK) return st;
-        if ((st = zero_fill(dD_vec, D, stream)) != MSS_OK) return st;
-        return zero_fill(dh0, BDN, stream);
-    }
-    s.bc_vec = N == 16 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
-               reinterpret_cast<uintptr_t>(C) % 16 == 0;
-    char* w = static_cast<char*>(workspace);
-    const mss::BwdArgs a{disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta, dA_log,
-                         dB, dC, dD_vec, z ? dz : nullptr, dh0,
-                         reinterpret_cast<float*>(w + lay.ckpt),
-                         reinterpret_cast<float*>(w + lay.partB),
-                         reinterpret_cast<float*>(w + lay.partC),
-                         reinterpret_cast<float*>(w + lay.partA),
-                         reinterpret_cast<float*>(w + lay.partD)};
-    const hipError_t e = mss::launch_scan_bwd(a, s, stream);
-    return e == hipSuccess ? MSS_OK : hip_fail(e);
+    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta,
+                           dA_log, dB, dC, dD_vec, dz, dh0, false, workspace, workspace_bytes,
+                           stream);
+}
+
+int mss_selective_scan_backward_noalloc(const mss_dims* dims, int disc, const float* u,
+                                        const float* delta, const float* A_log, const float* B,
+                                        const float* C, const float* D_vec, const float* z,
+                                        const float* h0, const float* dout, float* du,
+                                        float* ddelta, float* dA_log, float* dB, float* dC,
+                                        float* dD_vec, float* dz, float* dh0,
+                                        hipStream_t stream) {
+    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta,
+                           dA_log, dB, dC, dD_vec, dz, dh0, true, nullptr, 0, stream);
 }
 
 int mss_conv1d_silu_backward(const mss_dims* dims, const float* x, const float* w_conv,
@@ -661,6 +737,9 @@ const char* mss_strerror(int status) {
         case MSS_EALIAS: return "an output overlaps an input or another output";
         case MSS_EWORKSPACE: return "workspace missing or smaller than mss_workspace_bytes reports";
         case MSS_EHIP: return "HIP runtime error (see mss_last_hip_error)";
+        case MSS_ESCRATCH: return "the problem needs more scratch than the library's static "
+                                  "array holds (MSS_NOALLOC_SCRATCH_BYTES); use the entry point "
+                                  "with a caller workspace";
         default: return "unknown status";
     }
 }

@@ -327,3 +327,30 @@ def test_binding_loads_libmss_on_torchs_hip_runtime():
     assert r.returncode == 0, r.stderr[-2000:]
     libs = eval(r.stdout.strip().splitlines()[-1])
     assert len(libs) == 1 and "torch" in libs[0], libs
+
+
+def test_noalloc_backward_refuses_past_its_scratch(L):
+    """The allocation-free scan backward checks its size against the static
+    scratch array before any HIP call, so on a machine without a GPU a
+    request past MSS_NOALLOC_SCRATCH_BYTES comes back as MSS_ESCRATCH; bad
+    arguments are still reported first."""
+    assert re.search(r"#define MSS_NOALLOC_SCRATCH_BYTES \(256ull << 20\)", open(HEADER).read())
+    assert mss.NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert header_define("MSS_ESCRATCH") == mss.MSS_ESCRATCH
+    d = mss.make_dims(8, 2048, 1536, 16, 4)
+    assert ws_bytes(L, d, OP_SCAN_BWD)[1] > mss.NOALLOC_SCRATCH_BYTES
+
+    def call(dims, disc=0, **over):
+        args = dict(u=fake(1), delta=fake(2), A_log=fake(3), B=fake(4), C=fake(5),
+                    D_vec=fake(6), z=fake(7), h0=None, dout=fake(8), du=fake(9),
+                    ddelta=fake(10), dA_log=fake(11), dB=fake(12), dC=fake(13), dD=fake(14),
+                    dz=fake(15), dh0=None)
+        args.update(over)
+        return L.mss_selective_scan_backward_noalloc(ctypes.byref(dims), disc,
+                                                     *args.values(), None)
+
+    assert call(d) == mss.MSS_ESCRATCH
+    assert call(d, disc=3) == EINVAL
+    assert call(d, du=fake(1)) == EALIAS
+    assert call(d, dout=None) == EINVAL
+    assert b"static" in L.mss_strerror(mss.MSS_ESCRATCH)
