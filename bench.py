@@ -8,8 +8,12 @@ block, inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--disc zoh|euler] [--no-cpu-baseline]
 
-The default 20 warm-up calls (~20 ms) let the clock settle: under this
-VALU-heavy load it drops after the first few calls and recovers over ~20.
+Order of work: the side measurements on the GPU (the other workloads, the
+other discretisation, backward, SSD, decode) run first, then W warm-up steps
+and the K timed steps, then everything that times the CPU oracle.  Under
+this VALU-heavy load the clock settles over the first ~20 calls of a cold
+GPU; running the side measurements first lets the timed steps see the clock
+a continuously loaded GPU runs at.
 """
 from __future__ import annotations
 
@@ -47,11 +51,15 @@ def algorithmic_bytes(w) -> int:
     return 4 * (4 * M * D + 2 * M * N + D * N + D * (K + 2))
 
 
-# Non-packed fp32 VALU issue: 256 CUs x 4 SIMDs x 16 lanes per cycle x 2.4 GHz,
-# in lane operations per second (an FMA, multiply, add or transcendental is one
-# operation).  The published 157.3 TFLOP/s counts packed FMAs (two per lane,
-# two flops each), a form this library does not use.
+# Secondary roofline, VALU issue.  Non-packed fp32 issue: 256 CUs x 4 SIMDs x
+# 16 lanes per cycle x 2.4 GHz = 39.3e12 lane operations per second, where an
+# FMA, multiply or add takes one issue slot and a transcendental (exp, log,
+# rcp) two (measured: v_exp_f32 runs at half the FMA rate).  The published
+# 157.3 TFLOP/s fp32 vector peak counts packed FMAs (two per lane per cycle,
+# two flops each), a form this library does not use; the flops against it
+# are reported beside.
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def algorithmic_ops(w, disc) -> int:
@@ -64,6 +72,41 @@ def algorithmic_ops(w, disc) -> int:
     per_state = 7 if disc == "zoh" else 5
     per_md = K + 5 + 8 + 6 + 1 + (0 if disc == "zoh" else 1)
     return M * D * (N * per_state + per_md)
+
+
+def algorithmic_issue(w, disc):
+    """(issue slots, transcendentals, flops) per launch of the fused kernel:
+    the operations of algorithmic_ops with each transcendental taking a
+    second slot (per (m, d, n) one exp; per (m, d) two each in SiLU of the
+    conv, softplus and the gate), and flops with an FMA as two."""
+    M, D, N, K = w.M, w.d_inner, w.d_state, w.d_conv
+    ops = algorithmic_ops(w, disc)
+    trans = M * D * (N + 6)
+    # per (m, d, n): ZOH mul, exp, 2 mul, add, 2 FMA = 9 flops; EULER 7
+    per_state = 9 if disc == "zoh" else 7
+    per_md = 2 * K + 5 + 8 + 6 + 2 + (0 if disc == "zoh" else 1)
+    return ops + trans, trans, M * D * (N * per_state + per_md)
+
+
+def roofline(w, disc, kern_ms, traffic, digest):
+    """HBM roofline of the fused kernel (the metric's), with VALU issue beside."""
+    abytes = algorithmic_bytes(w)
+    achieved = abytes / (kern_ms / 1e3) / 1e9
+    issue, trans, flops = algorithmic_issue(w, disc)
+    ops = algorithmic_ops(w, disc)
+    t = kern_ms / 1e3
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "algorithmic_bytes": abytes, "kernel_ms": kern_ms, "kernel_digest": digest,
+            "alu": {"note": "secondary: the kernel is VALU-issue bound; peak = non-packed "
+                            "fp32 issue 256 CU x 4 SIMD x 16 lanes x 2.4 GHz, transcendentals "
+                            "at two slots",
+                    "algorithmic_ops": ops, "issue_slots": issue, "transcendentals": trans,
+                    "achieved_issue_T_per_s": issue / t / 1e12, "peak_T_per_s": ALU_PEAK_TOPS,
+                    "issue_frac": issue / t / 1e12 / ALU_PEAK_TOPS,
+                    "flops": flops, "achieved_TFLOPs": flops / t / 1e12,
+                    "published_fp32_vector_peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
+                    "frac_of_published_fp32_peak": flops / t / 1e12 / FP32_VECTOR_PEAK_TFLOPS}}
 
 
 def measured_traffic(digest: str):
@@ -130,7 +173,7 @@ def _stats(ts):
             "calls": len(ts)}
 
 
-def extras(w, inp, d, y, disc, stream, with_oracle=True):
+def extras(w, inp, d, y, disc, stream):
     """Side measurements: the other discretisation, the fused core reading
     column slices of the projection outputs, the unfused path (conv kernel,
     then the scan on u), and the decode workload (256 sequences x 5120
@@ -253,8 +296,9 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
 
     step_cold = _event_times(one_step, stream, 16, before=lambda: flush.fill_(1.0))
     del flush
-    res["backward"] = backward_extras(w, d, stream, with_oracle=with_oracle)
-    res["ssd"] = ssd_extras(stream, reps=10, with_oracle=with_oracle)
+    res["backward"] = backward_extras(w, d, stream, with_oracle=False)
+    res["ssd"] = ssd_extras(stream, reps=10, with_oracle=False)
+    res["workloads"] = workloads_extras(stream)
     BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
     step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
     res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
@@ -264,9 +308,70 @@ def extras(w, inp, d, y, disc, stream, with_oracle=True):
                      "graph_us_per_step": t64g * 1e3 / dw.seq_len,
                      "cold_us_per_step": _stats([t * 1e3 for t in step_cold]),
                      "cold_GBps": step_bytes / float(np.median(step_cold)) / 1e6}
-    if with_oracle:
-        res["cpu_oracle_1core"] = cpu_baseline(w, inp, disc, target_s=4.0, threads=1)
     return res
+
+
+def oracle_extras(w, inp, disc, extra):
+    """The CPU oracle's rates for the side measurements, after the GPU work."""
+    extra["cpu_oracle_1core"] = cpu_baseline(w, inp, disc, target_s=4.0, threads=1)
+    extra["backward"]["cpu_oracle"] = backward_oracle_rate(w)
+    from mamba_selective_scan_causal_amd import inputs as gen
+    sw = gen.SSD_2P7B
+    extra["ssd"]["cpu_oracle"] = ssd_oracle_rate(sw, gen.generate_ssd(sw))
+    for name, r in workloads_oracle().items():
+        extra["workloads"][name]["cpu_oracle_1core"] = r
+
+
+def workload_bytes(w, h_cache: bool) -> int:
+    """Algorithmic bytes of a fused call: algorithmic_bytes, plus the state
+    cache (4 N bytes per (m, d)) when it is written."""
+    return algorithmic_bytes(w) + (4 * w.M * w.d_inner * w.d_state if h_cache else 0)
+
+
+def workloads_extras(stream, reps=50):
+    """The fused core on the other sequence workloads (1 x 64 x 32 with the
+    clamp path, 2 x 512 x 256 and 8 x 2048 x 1536): both discretisations,
+    with the state cache where the workload emits it; median of `reps`
+    event-timed calls after a warm-up."""
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+    out = {}
+    for w in (gen.TINY_CLAMP, gen.SMALL, gen.MAMBA_130M):
+        inp = gen.generate(w)
+        d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+        y = torch.empty((w.M, w.d_inner), device="cuda")
+        hc = (torch.empty((w.batch, w.seq_len, w.d_inner, w.d_state), device="cuda")
+              if w.hcache else False)
+        res = {"h_cache": w.hcache}
+        for disc in ("zoh", "euler"):
+            def f(disc=disc):
+                mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"],
+                                d["B"], d["C"], d["D_vec"], d["z"], None, batch=w.batch,
+                                seq_len=w.seq_len, disc=disc, out=y, h_cache=hc, stream=stream)
+            _event_times(f, stream, 20)
+            ts = _event_times(f, stream, reps)
+            ms = float(np.median(ts))
+            nb = workload_bytes(w, w.hcache)
+            res[disc] = {"ms": ms, "min_ms": float(np.min(ts)),
+                         "elements_per_s": w.M * w.d_inner / (ms / 1e3),
+                         "algorithmic_bytes": nb, "GBps": nb / ms / 1e6,
+                         "frac_of_hbm_peak": nb / ms / 1e6 / HBM_PEAK_GBS}
+        out[w.name] = res
+        del d, y, hc
+    return out
+
+
+def workloads_oracle(target_s=3.0):
+    """The oracle as it stands on one core on the same workloads (whole
+    workload for the two small ones, a bounded sample of whole columns of
+    the 8 x 2048 x 1536 one), ZOH."""
+    from mamba_selective_scan_causal_amd import inputs as gen
+    out = {}
+    for w in (gen.TINY_CLAMP, gen.SMALL, gen.MAMBA_130M):
+        inp = gen.generate(w)
+        out[w.name] = cpu_baseline(w, inp, "zoh", target_s=target_s, threads=1)
+    return out
 
 
 def backward_extras(w, d, stream, reps=5, with_oracle=True):
@@ -432,9 +537,10 @@ def main():
                     help="skip the side measurements (other mode, unfused path, decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--part", default="all", choices=("all", "backward", "ssd"),
+    ap.add_argument("--part", default="all", choices=("all", "backward", "ssd", "workloads"),
                     help="backward: only the backward passes on the same workload; ssd: only "
-                         "the Mamba-2 SSD scan (one JSON line of timings, for profiling)")
+                         "the Mamba-2 SSD scan; workloads: only the fused core on the three "
+                         "smaller workloads (one JSON line of timings, for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
@@ -449,6 +555,13 @@ def main():
     import mamba_selective_scan_causal_amd as mss
     from mamba_selective_scan_causal_amd import inputs as gen
 
+    if args.part == "workloads":
+        r = workloads_extras(torch.cuda.current_stream(), reps=max(args.steps, 1))
+        if not args.no_cpu_baseline:
+            for name, o in workloads_oracle().items():
+                r[name]["cpu_oracle_1core"] = o
+        print(json.dumps(r))
+        return
     w = gen.MAMBA_2P8B
     inp = gen.generate(w)
     d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
@@ -470,6 +583,9 @@ def main():
                         d["D_vec"], d["z"], None, batch=w.batch, seq_len=w.seq_len,
                         disc=args.disc, out=y, stream=stream)
 
+    extra = None
+    if not args.no_extras:
+        extra = extras(w, inp, d, y, args.disc, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -487,12 +603,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     elems = w.M * w.d_inner
     value = elems / (ms_per_step / 1e3)
-
-    abytes = algorithmic_bytes(w)
-    ops = algorithmic_ops(w, args.disc)
-    achieved = abytes / (kern_ms / 1e3) / 1e9
     digest = kernel_digest()
-    traffic = measured_traffic(digest)
     out = {
         "metric": METRIC,
         "value": value,
@@ -509,21 +620,16 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
                    "d_inner": w.d_inner, "d_state": w.d_state, "d_conv": w.d_conv,
                    "disc": args.disc, "h_cache": False, "kernel": "mss_mamba1_core (fused)"},
-        # The fused kernel is bound by VALU issue (one exp and ~6 FMA-class
-        # operations per (m, d, n)), not by HBM: the roofline is the ALU one;
-        # the HBM figures of the metric are kept beside it.
-        "roofline": {"bound": "alu", "achieved": ops / (kern_ms / 1e3) / 1e12,
-                     "peak": ALU_PEAK_TOPS, "unit": "Top/s",
-                     "frac": ops / (kern_ms / 1e3) / 1e12 / ALU_PEAK_TOPS, "traffic": traffic,
-                     "kernel_ms": kern_ms, "algorithmic_ops": ops,
-                     "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": abytes},
-                     "kernel_digest": digest},
+        # The metric's roofline: algorithmic HBM bytes over the mean event
+        # time of the fused kernel, against 8 TB/s.  The kernel is bound by
+        # VALU issue; that fraction is in roofline.alu.
+        "roofline": roofline(w, args.disc, kern_ms, measured_traffic(digest), digest),
         "kernel_ms": _stats(kern_times),
     }
-    if not args.no_extras:
-        out["extra"] = extras(w, inp, d, y, args.disc, stream,
-                              with_oracle=not args.no_cpu_baseline)
+    if extra is not None:
+        if not args.no_cpu_baseline:
+            oracle_extras(w, inp, args.disc, extra)
+        out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.disc)
     print(json.dumps(out), flush=True)

@@ -41,3 +41,17 @@ def test_traffic_only_for_the_measured_kernel_source():
 def _bench_workload():
     from mamba_selective_scan_causal_amd import inputs as gen
     return gen.MAMBA_2P8B
+
+
+def test_roofline_is_the_hbm_one():
+    """roofline.frac is algorithmic bytes / kernel time / 8 TB/s (the
+    metric's roofline); the VALU issue figures sit under roofline.alu."""
+    w = _bench_workload()
+    r = bench.roofline(w, "zoh", 1.0, None, "x")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert bench.algorithmic_bytes(w) == 2688999424
+    assert abs(r["achieved"] - 2688999424 / 1e-3 / 1e9) < 1e-6
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-12
+    a = r["alu"]
+    assert a["issue_slots"] == a["algorithmic_ops"] + a["transcendentals"]
+    assert 0.0 < a["frac_of_published_fp32_peak"] < a["issue_frac"]
