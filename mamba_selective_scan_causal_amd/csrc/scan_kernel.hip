@@ -22,19 +22,15 @@
 // Parallelism over time.  The B * ceil(D/64) column tiles alone give too few
 // waves for 1024 SIMDs, so the flattened (tile, t) space is cut into equal
 // segments, one per wave.  A segment that starts at t0 > 0 needs the state
-// h(t0 - 1).  Because the recurrence forgets exponentially -- the part of
-// h(t0-1) that comes from before step s is multiplied by
-// prod_{r=s}^{t0-1} aBar_r = exp(A_n * sum_r dv_r) -- the wave first walks
-// delta backwards from t0 - 1 until sum dv * min_n |A_n| >= c ln 2 holds in
-// every lane (c = MSS_REPLAY_DECAY_BITS, or t = 0 is reached), then replays
-// the recurrence forward from that step with h = 0 (state only, no
-// outputs).  What this drops is exactly the state at the replay start times
-// a factor <= 2^-c per state -- small against the outputs unless that state
-// is ~2^c / 10^4 times larger than they are; reaching t = 0 makes it exact.
-// States that decay faster than the slowest one join the replay later, each
-// once its own decay to t0 reaches the same bound.  MSS_FLAG_EXACT makes
-// every segment a whole tile (no replay).  No workspace and no inter-wave
-// synchronisation.
+// h(t0 - 1) = sum_{s < t0} (prod_{r=s+1}^{t0-1} aBar_r) bBar_s u_s.  The
+// recurrence forgets exponentially, so the wave sums these terms newest
+// first, keeping each state's decay product q, and stops a state at the
+// first 8-step block boundary where its q is below 2^-c in every lane
+// (c = MSS_REPLAY_DECAY_BITS).  What that leaves out is q times the state
+// before that step: small against the outputs unless that state is far
+// larger than they are (~2^c / 10^4 times); reaching t = 0 (with h0) makes
+// it exact.  MSS_FLAG_EXACT makes every segment a whole tile (no replay).
+// No workspace and no inter-wave synchronisation.
 #include "device_math.h"
 #include "launch.h"
 
@@ -42,8 +38,9 @@ namespace mss {
 namespace {
 
 constexpr int kT = 8;                         // steps per straight-line block
-constexpr int kBackBlk = 16;                  // delta loads in flight in the backward walk
-constexpr float kDecayCut = MSS_REPLAY_DECAY_BITS;   // replay until the carried part has decayed this many bits
+// A state's replay stops once its decay to the segment start is below 2^-c.
+constexpr float pow2_neg(int c) { return c <= 0 ? 1.0f : 0.5f * pow2_neg(c - 1); }
+constexpr float kDropQ = pow2_neg(MSS_REPLAY_DECAY_BITS);
 // Below |dv*A| = 2^-6 the decay is applied through expm1 (see step()).
 constexpr float kSmallX = 0.015625f;
 constexpr float kSmallX2 = kSmallX * kLog2e;  // the same bound in log2 units
@@ -144,30 +141,6 @@ struct Scan {
             ln.bias = c.b_conv ? c.b_conv[d] : 0.0f;
 #pragma unroll
             for (int k = 0; k < KR; k++) ln.w[k] = (KS > 0 || k < K) ? c.w_conv[d * K + k] : 0.0f;
-        }
-    }
-
-    // First step of the forward replay: pick it by walking delta backwards.
-    // S returns the lane's sum of dv over [start, t0).
-    __device__ __forceinline__ int64_t replay_start(const L_t& ln, int64_t t0, float& S) const {
-        S = 0.0f;
-        if (t0 == 0) return 0;
-        int64_t t = t0;  // next step to visit is t - 1
-        while (true) {
-            float dd[kBackBlk];
-#pragma unroll
-            for (int i = 0; i < kBackBlk; i++) {
-                const int64_t tt = t - 1 - i;
-                dd[i] = ld(c.delta, ldd, tt >= 0 ? tt : 0);
-            }
-#pragma unroll
-            for (int i = 0; i < kBackBlk; i++) {
-                const int64_t tt = t - 1 - i;
-                if (tt < 0) return 0;
-                S += softplus(dd[i]);
-                if (wave_all(S * ln.min_a2 >= kDecayCut)) return tt;
-            }
-            t -= kBackBlk;
         }
     }
 
@@ -421,89 +394,174 @@ struct Scan {
         }
     }
 
-    // Replay of steps [tb, te), state only; S = the lane's sum of dv over
-    // [tb, te).  The replay start was chosen for the slowest state; a faster
-    // state n joins only at the last block start from which its own decay
-    // to te, 2^(-|A2_n| sum dv), is still <= 2^-c in every lane, and is 0
-    // until then.  That drops no more than the replay start itself drops, at
-    // a fraction of the cost when the decay rates differ (|A| = 1..16 makes
-    // the replay ~4x cheaper).  A replay from t = 0 is exact: every state
-    // runs from the start.
-    __device__ __forceinline__ void warm(L_t& ln, int64_t tb, int64_t te, float S) const {
-        if (tb >= te) return;
-        if constexpr (!kStage) {
-            sweep<kWarm>(ln, tb, te);
-        } else {
-            constexpr uint32_t kAll = (1u << NR) - 1u;
-            uint32_t act = tb == 0 ? kAll : 0u;   // wave-uniform set of running states
-            // S is kept by subtraction; slack bounds the rounding of the
-            // walk's sum and of the subtractions ((2 R + 16) u S over R
-            // steps), so S - slack is a lower bound of the exact remainder.
-            const float slack = S * (2.0f * static_cast<float>(te - tb) + 16.0f) * 0x1p-24f;
-            const float* ldsf = reinterpret_cast<const float*>(lds);
-            float nx[kT], nd[kT], nz[kT];
-            float4 nbc = load_bc(tb);
-            load_block<kWarm>(nx, nd, nz, tb);
-            int64_t t = tb;
-            for (; t + kT <= te; t += kT) {
-                float cx[kT], dv[kT];
-                float sdv = 0.0f;
+    // ---- the state a segment starts from -------------------------------
+    // h(t0-1) = sum_{s < t0} q_s bBar_s u_s + q_{-1} h0 with
+    // q_s = prod_{r=s+1}^{t0-1} aBar_r, accumulated newest step first: q is
+    // a running product per state, and state n stops at the first block
+    // boundary where q_n < 2^-c in every lane -- what it leaves out is q_n
+    // times the state before that step, at most 2^-c of it.  ZOH terms are
+    // q (aBar - 1) u B / A: the running sum takes q (aBar - 1) u B and 1/A
+    // multiplies it once at the end.  Blocks of kT steps are counted back
+    // from t0, the loads of the next block in flight while one is summed
+    // (two in flight pushed the kernel past 256 VGPRs into scratch);
+    // reaching t = 0 adds the decayed h0 and is exact.
+
+    // Inputs of the block [tb, tb + kT) (tb may be negative for the block
+    // that reaches the sequence start): src at tb-(KR-1) .. tb+kT-1 (zero
+    // before t = 0), delta at tb .. tb+kT-1, and (N = 16, staged) this
+    // lane's 16 bytes of the block's B rows (lanes 0-31 hold them).
+    struct RBlock {
+        float xh[kT + KR - 1];
+        float dd[kT];
+        float4 bq;
+    };
+
+    __device__ __forceinline__ void rload(RBlock& r, int64_t tb) const {
 #pragma unroll
-                for (int i = 0; i < kT; i++) {
-                    cx[i] = nx[i];
-                    dv[i] = softplus(nd[i]);
-                    sdv += dv[i];
+        for (int j = 0; j < kT + KR - 1; j++) {
+            const int64_t t = tb - (KR - 1) + j;
+            const int64_t tc = t < 0 ? 0 : (t < L ? t : L - 1);
+            const float v = ld(c.src, ldx, tc);
+            r.xh[j] = t >= 0 ? v : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            const int64_t t = tb + i;
+            r.dd[i] = ld(c.delta, ldd, t < 0 ? 0 : (t < L ? t : L - 1));
+        }
+        if constexpr (kStage) {
+            const uint32_t q = threadIdx.x & 31u;
+            int64_t t = tb + static_cast<int64_t>(q >> 2);
+            t = t < 0 ? 0 : (t < L ? t : L - 1);
+            r.bq = *reinterpret_cast<const float4*>(c.Bm + row(t) * ldB + (q & 3u) * 4);
+        }
+    }
+
+    // One block of the replay, newest step first.  FULL: no step before t = 0.
+    // LAST: the block that reaches t = 0 (no state stops after it).
+    template <bool FULL>
+    __device__ __forceinline__ void rblock(const L_t& ln, const RBlock& r, int64_t tb,
+                                           float (&q)[NR], float (&g)[NR], uint32_t& act,
+                                           bool last) const {
+        float dv[kT], w[kT];   // w: EULER dv u, ZOH u
+        float sdv = 0.0f;
+        int nst = 0;
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            if (FULL || tb + i >= 0) {
+                dv[i] = softplus(r.dd[i]);
+                float u;
+                if constexpr (kFused) {
+                    float acc = __builtin_fmaf(ln.w[0], r.xh[i + KR - 1], ln.bias);
+#pragma unroll
+                    for (int k = 1; k < KR; k++)
+                        if (KS > 0 || k < K) acc = __builtin_fmaf(ln.w[k], r.xh[i + KR - 1 - k], acc);
+                    u = silu(acc);
+                } else {
+                    u = r.xh[i];
                 }
-                lds[threadIdx.x] = nbc;
-                load_block<kWarm>(nx, nd, nz, t + kT);
-                nbc = load_bc(t + kT);
-                S -= sdv;   // remainder after this block
-                if (act != kAll) {
-                    // Written as "not provably decayed enough", so that a
-                    // non-finite sum (an infinite delta makes S - slack NaN)
-                    // lets the state join.
+                w[i] = DISC == MSS_DISC_EULER ? dv[i] * u : u;
+                sdv += dv[i];
+                nst++;
+            } else {
+                dv[i] = 0.0f;
+                w[i] = 0.0f;
+            }
+        }
+        // The accurate form when the block's decay is weak in some lane, as
+        // in the sweep: q (aBar - 1) from m = expm1(dv A) instead of q aBar - q.
+        const bool slow = wave_any(sdv * ln.min_a2 < static_cast<float>(nst) * kSmallX2);
+        if (!slow)
+            rstates<FULL, false>(ln, tb, dv, w, q, g, act, last);
+        else
+            rstates<FULL, true>(ln, tb, dv, w, q, g, act, last);
+    }
+
+    // The states of one replay block (the block's inputs already reduced to
+    // dv and w); ACC: the accurate form.
+    template <bool FULL, bool ACC>
+    __device__ __forceinline__ void rstates(const L_t& ln, int64_t tb, const float (&dv)[kT],
+                                            const float (&w)[kT], float (&q)[NR], float (&g)[NR],
+                                            uint32_t& act, bool last) const {
+        const float* ldsf = reinterpret_cast<const float*>(lds);
 #pragma unroll
-                    for (int n = 0; n < NR; n++)
-                        if (!(act & (1u << n)) &&
-                            wave_any(!((S - slack) * -ln.A2[n] >= kDecayCut + 0.25f)))
-                            act |= 1u << n;
+        for (int n = 0; n < NR; n++) {
+            if (!(act & (1u << n))) continue;
+            float qq = q[n], gg = g[n];
+#pragma unroll
+            for (int i = kT - 1; i >= 0; i--) {
+                if (!FULL && tb + i < 0) continue;
+                float Bv;
+                if constexpr (kStage) {
+                    Bv = ldsf[i * 16 + n];
+                } else {
+                    Bv = as_const(c.Bm + row(tb + i) * ldB)[n];
                 }
-                if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {
-                    float w[kT];   // EULER: dv u; ZOH: u
-#pragma unroll
-                    for (int i = 0; i < kT; i++) {
-                        const float u = scan_input(ln, cx[i]);
-                        w[i] = DISC == MSS_DISC_EULER ? dv[i] * u : u;
-                    }
-                    // State-major: each running state takes the block's 8
-                    // steps in a row (B_t[n] of step i is float i*16 + n).
-#pragma unroll
-                    for (int n = 0; n < NR; n++) {
-                        if (act & (1u << n)) {
-#pragma unroll
-                            for (int i = 0; i < kT; i++) {
-                                const float Bv = ldsf[i * 16 + n];
-                                const float a = ex2(dv[i] * ln.A2[n]);
-                                if constexpr (DISC == MSS_DISC_EULER) {
-                                    ln.h[n] = __builtin_fmaf(a, ln.h[n], w[i] * Bv);
-                                } else {
-                                    const float k = (w[i] * ln.Ai[n]) * Bv;
-                                    ln.h[n] = __builtin_fmaf(a, ln.h[n] + k, -k);
-                                }
-                            }
-                        }
+                const float x2 = dv[i] * ln.A2[n];
+                const float a = ex2(x2);
+                if constexpr (!ACC) {
+                    if constexpr (DISC == MSS_DISC_EULER) {
+                        gg = __builtin_fmaf(qq, w[i] * Bv, gg);
+                        qq *= a;
+                    } else {
+                        const float qn = qq * a;
+                        gg = __builtin_fmaf(qn - qq, w[i] * Bv, gg);
+                        qq = qn;
                     }
                 } else {
-                    // the accurate path for every state (a state that had not
-                    // joined starts early, from 0: only more exact)
-                    steps1<kWarm, true>(ln, t, kT);
-                    act = kAll;
+                    const float x = x2 * kLn2;
+                    const float p = x * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 6.0f, 0.5f), 1.0f);
+                    const float m = __builtin_fabsf(x) < kSmallX ? p : a - 1.0f;
+                    const float dq = qq * m;
+                    if constexpr (DISC == MSS_DISC_EULER)
+                        gg = __builtin_fmaf(qq, w[i] * Bv, gg);
+                    else
+                        gg = __builtin_fmaf(dq, w[i] * Bv, gg);
+                    qq += dq;
                 }
             }
-            if (t < te) {
-                lds[threadIdx.x] = nbc;
-                steps1<kWarm, true>(ln, t, static_cast<int>(te - t));
-            }
+            q[n] = qq;
+            g[n] = gg;
+            // Stop the state once its decay to t0 is below the cut in every
+            // lane (a NaN never compares below: such a column runs to t = 0).
+            if (!last && wave_all(qq < kDropQ)) act &= ~(1u << n);
+        }
+    }
+
+    __device__ __forceinline__ void rebuild(L_t& ln, int64_t t0) const {
+        float q[NR], g[NR];
+        uint32_t act = 0;
+#pragma unroll
+        for (int n = 0; n < NR; n++) {
+            q[n] = 1.0f;
+            g[n] = 0.0f;
+            if (NS > 0 || n < N) act |= 1u << n;
+        }
+        RBlock nxt;
+        int64_t tb = t0 - kT;
+        rload(nxt, tb);
+        while (true) {
+            // the block at tb; the loads of the one before it go out first
+            if constexpr (kStage)
+                if (threadIdx.x < 32) lds[threadIdx.x] = nxt.bq;
+            const RBlock cur = nxt;
+            if (tb > 0) rload(nxt, tb - kT);
+            if (tb >= 0)
+                rblock<true>(ln, cur, tb, q, g, act, tb == 0);
+            else
+                rblock<false>(ln, cur, tb, q, g, act, true);
+            if (tb <= 0 || !act) break;
+            tb -= kT;
+        }
+        // states still running here took every step down to t = 0
+        const bool start = tb <= 0;
+#pragma unroll
+        for (int n = 0; n < NR; n++) {
+            if (!(NS > 0 || n < N)) continue;
+            float h = DISC == MSS_DISC_EULER ? g[n] : g[n] * ln.Ai[n];
+            if (start && c.h0 && (act & (1u << n)))
+                h = __builtin_fmaf(q[n], c.h0[(b * D + d) * N + n], h);
+            ln.h[n] = h;
         }
     }
 
@@ -511,15 +569,14 @@ struct Scan {
     __device__ __forceinline__ void run(int64_t t0, int64_t t1) const {
         L_t ln;
         init(ln);
-        float S;
-        const int64_t tw = replay_start(ln, t0, S);
-        if (tw == 0 && c.h0) {
+        if (t0 > 0) {
+            rebuild(ln, t0);
+        } else if (c.h0) {
 #pragma unroll
             for (int n = 0; n < NR; n++)
                 if (NS > 0 || n < N) ln.h[n] = c.h0[(b * D + d) * N + n];
         }
-        load_window(ln, tw);
-        warm(ln, tw, t0, S);
+        load_window(ln, t0);
         if constexpr (HC)
             sweep<kOutHC>(ln, t0, t1);
         else

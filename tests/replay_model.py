@@ -1,10 +1,11 @@
 """CPU model of what the time split of the scans leaves out, for tests.
 
 The HIP scans process time in segments; a segment that starts at t0 > 0
-rebuilds its starting state by replaying the recurrence from h = 0 at a step
-chosen from delta alone.  That choice is a rule on fp32 sums of softplus(delta)
-(the kernels' own rule, restated here in numpy), and what it drops is a
-closed form of the fp64 oracle's states:
+rebuilds its starting state from the steps before it, going back only until
+their weight has decayed below 2^-cut.  Where each state's replay starts is
+a rule on fp32 decay products or sums of softplus(delta) (the kernels' own
+rules, restated here in numpy), and what it drops is a closed form of the
+fp64 oracle's states:
 
     state n of column d at t >= t0 lacks  E_n(t) = prod_{s=tj_n..t} aBar_s[n] * h_{tj_n - 1}[n]
 
@@ -49,7 +50,8 @@ def segment_starts(tile: int, L: int, seg: int):
 
 
 def replay_start(dv32: np.ndarray, min_a2: np.ndarray, t0: int, cut: float):
-    """Backward walk from t0 - 1: the first step tt at which
+    """The scan backward's forward-state replay (and the SSD scan's, per
+    head): backward walk from t0 - 1 to the first step tt at which
     S = sum_{s=tt}^{t0-1} dv_s satisfies S * min_a2 >= cut in every lane,
     or 0.  dv32: (L, lanes) fp32; min_a2: (lanes,) fp32.  Returns (tt, S)."""
     S = np.zeros(dv32.shape[1], dtype=np.float32)
@@ -73,37 +75,36 @@ def replay_end(dv32: np.ndarray, min_a2: np.ndarray, t1: int, cut: float) -> int
     return L
 
 
-def join_steps(dv32: np.ndarray, A2: np.ndarray, tw: int, S: np.ndarray, t0: int,
-               cut: float) -> np.ndarray:
-    """Replay start of every state (N,) in the forward kernel with N = 16:
-    the slowest state starts at tw; a faster one joins at the first 8-step
-    block from whose end its own remaining decay to t0 is not provably at
-    least cut + 1/4 bits in every lane (the sum is kept by subtraction, with
-    a bound on its rounding taken off first), or wherever a block needs the
-    accurate path or the replay's last partial block begins (all states run
-    there).  A replay from t = 0 runs every state from the start."""
-    N = A2.shape[1]
-    if tw == 0:
-        return np.zeros(N, dtype=np.int64)
-    lanes = dv32.shape[1]
-    S = S.astype(np.float32).copy()             # the walk's sum over [tw, t0)
-    slack = (S * np.float32(2.0 * (t0 - tw) + 16.0) * np.float32(2.0 ** -24)).astype(np.float32)
-    min_a2 = (-A2).min(axis=1).astype(np.float32)
-    join = np.full(N, -1, dtype=np.int64)
-    t = tw
-    while t + BLOCK <= t0:
-        sdv = np.zeros(lanes, dtype=np.float32)
-        for i in range(BLOCK):
-            sdv = (sdv + dv32[t + i]).astype(np.float32)
-        S = (S - sdv).astype(np.float32)
+def forward_replay_starts(dv32: np.ndarray, A2: np.ndarray, t0: int, cut: float) -> np.ndarray:
+    """First step of every state's replay (N,) in the forward kernel: the
+    kernel accumulates the state entering t0 newest step first, in blocks of
+    8 counted back from t0, keeping the decay to t0 as a running fp32
+    product q; state n stops after the first block (short of t = 0) at whose
+    start q_n < 2^-cut in every lane.  States that never stop start at 0."""
+    lanes, N = A2.shape
+    q = np.ones((lanes, N), dtype=np.float32)
+    thr = np.float32(2.0 ** -cut)
+    start = np.zeros(N, dtype=np.int64)
+    active = np.ones(N, dtype=bool)
+    tb = t0 - BLOCK
+    while True:
+        for i in range(BLOCK - 1, -1, -1):
+            t = tb + i
+            if t < 0:
+                continue
+            a = np.exp2((dv32[t][:, None] * A2).astype(np.float32)).astype(np.float32)
+            q[:, active] = (q[:, active] * a[:, active]).astype(np.float32)
+        if tb <= 0:
+            break
         for n in range(N):
-            if join[n] < 0 and np.any(~(((S - slack) * -A2[:, n]) >= np.float32(cut + 0.25))):
-                join[n] = t
-        if np.any(sdv * min_a2 < np.float32(BLOCK) * SMALL_X2):
-            join[join < 0] = t
-        t += BLOCK
-    join[join < 0] = t        # the last partial block (or t0) runs every state
-    return join
+            if active[n] and np.all(q[:, n] < thr):
+                active[n] = False
+                start[n] = tb
+        if not active.any():
+            break
+        tb -= BLOCK
+    start[active] = 0
+    return start
 
 
 def forward_dropped(u, delta, A_log, B, C, z, *, L: int, b: int, d0: int, t0: int,
@@ -122,9 +123,8 @@ def forward_dropped(u, delta, A_log, B, C, z, *, L: int, b: int, d0: int, t0: in
     A2 = a2_of(A_log[cols])                        # (64, N)
     dv32 = softplus32(delta[rows, cols])          # (L, 64)
     dv64 = np.logaddexp(0.0, delta[rows, cols].astype(np.float64))
-    min_a2 = (-A2).min(axis=1).astype(np.float32)
-    tw, S = replay_start(dv32, min_a2, t0, cut)
-    join = join_steps(dv32, A2, tw, S, t0, cut)
+    join = forward_replay_starts(dv32, A2, t0, cut)
+    tw = int(join.min())
     A = -np.exp(np.clip(A_log[cols].astype(np.float64), -10.0, 5.0))   # (64, N)
     T = t_end - t0
     E = np.zeros((TILE_FWD, T, A.shape[1]))
