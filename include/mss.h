@@ -89,6 +89,16 @@ extern "C" {
  * SSD scan). */
 #define MSS_REPLAY_DECAY_BITS 24
 #define MSS_FLAG_EXACT 1
+/* MSS_FLAG_CKPT8: state checkpoints every 8 steps, for the backward pass.
+ * Forward calls: h_cache is (B, ceil(L/8), D, N) and holds the state entering
+ * steps 0, 8, 16, ... (entry k = h_{8k-1}; entry 0 = h0, or 0) instead of
+ * every step's state -- 8 bytes per (m, d) instead of 64.
+ * mss_selective_scan_backward: the flag says that h_ckpt carries those
+ * checkpoints (from a forward call with the same inputs); the backward then
+ * starts every 8-step block from them instead of rebuilding the states, and
+ * needs no checkpoint workspace (mss_workspace_bytes with the flag set
+ * reports the smaller size).  Without the flag h_ckpt must be NULL. */
+#define MSS_FLAG_CKPT8 2
 typedef struct mss_dims {
     int32_t struct_size;
     int32_t flags;          /* 0, or MSS_FLAG_EXACT (any other bit: MSS_EINVAL) */
@@ -231,13 +241,15 @@ int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes);
  * starting point has decayed by 2^-MSS_REPLAY_DECAY_BITS (see "Time split";
  * for the adjoint the window runs forward in time from the segment end).
  * MSS_FLAG_EXACT: no split, no replay.                                      */
+/* h_ckpt (B, ceil(L/8), D, N): the forward's states entering every 8th step
+ * (MSS_FLAG_CKPT8 in dims->flags; NULL otherwise).                        */
 int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 const float* delta, const float* A_log, const float* B,
                                 const float* C, const float* D_vec, const float* z,
-                                const float* h0, const float* dout, float* du, float* ddelta,
-                                float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
-                                float* dh0, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const float* h0, const float* h_ckpt, const float* dout,
+                                float* du, float* ddelta, float* dA_log, float* dB, float* dC,
+                                float* dD_vec, float* dz, float* dh0, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving or training loops, harnesses that forbid hipMalloc:
@@ -261,9 +273,9 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
 int mss_selective_scan_backward_noalloc(const mss_dims* dims, int disc, const float* u,
                                         const float* delta, const float* A_log, const float* B,
                                         const float* C, const float* D_vec, const float* z,
-                                        const float* h0, const float* dout, float* du,
-                                        float* ddelta, float* dA_log, float* dB, float* dC,
-                                        float* dD_vec, float* dz, float* dh0,
+                                        const float* h0, const float* h_ckpt, const float* dout,
+                                        float* du, float* ddelta, float* dA_log, float* dB,
+                                        float* dC, float* dD_vec, float* dz, float* dh0,
                                         hipStream_t stream);
 
 /* Gradients of u = SiLU(conv1d(x)) (mss_conv1d_silu) against du (M, D), the
@@ -317,8 +329,10 @@ int mss_ssd_scan(const mss_ssd_dims* dims, int disc, const float* x, const float
  * their strided forms) or MSS_OP_SELECTIVE_SCAN_BACKWARD.  The scans cut the
  * flattened (tile, t) space, tile = b * ceil(D/T) + d / T with T = 64
  * channels (forward) or 32 (backward) and t running fastest, into pieces of
- * *segment_steps steps; a segment starts wherever (tile * L + t) is a
- * multiple of *segment_steps.  0 for empty problems.                        */
+ * *segment_steps steps (a multiple of 8); a segment starts wherever
+ * (tile * Lp + t) is a multiple of *segment_steps, with Lp = L rounded up to
+ * a multiple of 8 (so segments start at multiples of 8).  0 for empty
+ * problems.                                                                 */
 #define MSS_OP_SELECTIVE_SCAN 3
 int mss_time_split(const mss_dims* dims, int op, int64_t* segment_steps);
 

@@ -45,11 +45,12 @@ class Dims(ctypes.Structure):
 
 
 FLAG_EXACT = 1          # no time split: the plain sequential recurrence
+FLAG_CKPT8 = 2          # state checkpoints every 8 steps (forward h_cache / backward h_ckpt)
 
 
-def make_dims(batch, seq_len, d_inner, d_state, d_conv=1, exact=False) -> Dims:
-    return Dims(ctypes.sizeof(Dims), FLAG_EXACT if exact else 0, batch, seq_len, d_inner,
-                d_state, d_conv)
+def make_dims(batch, seq_len, d_inner, d_state, d_conv=1, exact=False, ckpt8=False) -> Dims:
+    flags = (FLAG_EXACT if exact else 0) | (FLAG_CKPT8 if ckpt8 else 0)
+    return Dims(ctypes.sizeof(Dims), flags, batch, seq_len, d_inner, d_state, d_conv)
 
 
 class Strides(ctypes.Structure):
@@ -114,8 +115,8 @@ def lib():
         L.mss_mamba1_core_strided.argtypes = [dp, sp, i] + [p] * 14
         sz = ctypes.c_size_t
         L.mss_workspace_bytes.argtypes = [dp, i, ctypes.POINTER(sz)]
-        L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 18 + [sz, p]
-        L.mss_selective_scan_backward_noalloc.argtypes = [dp, i] + [p] * 17
+        L.mss_selective_scan_backward.argtypes = [dp, i] + [p] * 19 + [sz, p]
+        L.mss_selective_scan_backward_noalloc.argtypes = [dp, i] + [p] * 18
         L.mss_conv1d_silu_backward.argtypes = [dp] + [p] * 8 + [sz, p]
         L.mss_ssd_scan.argtypes = [ctypes.POINTER(SsdDims), i] + [p] * 11
         L.mss_time_split.argtypes = [dp, i, ctypes.POINTER(ctypes.c_int64)]
@@ -226,27 +227,36 @@ def conv1d_silu(x, w_conv, b_conv=None, *, batch, seq_len, out=None, stream=None
     return u
 
 
-def _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last):
+def ckpt_steps(seq_len) -> int:
+    """Rows of an 8-step checkpoint tensor: ceil(seq_len / 8)."""
+    return (seq_len + 7) // 8
+
+
+def _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last, ckpt8=False):
     M = batch * seq_len
     y = out if out is not None else _empty((M, D), x)
+    Lc = ckpt_steps(seq_len) if ckpt8 else seq_len
     hc = (h_cache if not isinstance(h_cache, bool) else
-          (_empty((batch, seq_len, D, N), x) if h_cache else None))
+          (_empty((batch, Lc, D, N), x) if h_cache else None))
     hl = (h_last if not isinstance(h_last, bool) else
           (_empty((batch, D, N), x) if h_last else None))
     return y, hc, hl
 
 
 def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch, seq_len, disc,
-                   h_cache=False, h_last=False, out=None, stream=None, exact=False):
+                   h_cache=False, h_last=False, out=None, stream=None, exact=False, ckpt8=False):
     """Selective scan + gate on a given u.  Returns (y, h_cache, h_last).
 
     ``h_cache`` / ``h_last``: False (skip), True (allocate) or an output tensor.
     u, delta, z, B, C and ``out`` may be row-strided views (column slices).
-    ``exact``: no time split (the plain sequential recurrence, less parallel)."""
+    ``exact``: no time split (the plain sequential recurrence, less parallel).
+    ``ckpt8``: h_cache is (batch, ceil(seq_len/8), D, N), the state entering
+    steps 0, 8, 16, ... (the backward's checkpoints)."""
     D, N = A_log.shape
     M = batch * seq_len
-    y, hc, hl = _scan_outputs(u, batch, seq_len, D, N, out, h_cache, h_last)
-    dims = make_dims(batch, seq_len, D, N, 1, exact)
+    Lc = ckpt_steps(seq_len) if ckpt8 else seq_len
+    y, hc, hl = _scan_outputs(u, batch, seq_len, D, N, out, h_cache, h_last, ckpt8)
+    dims = make_dims(batch, seq_len, D, N, 1, exact, ckpt8)
     common = (_ptr(A_log, "A_log", (D, N)),)
     tail = (_ptr(D_vec, "D_vec", (D,), False),)
     if _dense(u, delta, B, C, z, y):
@@ -254,7 +264,7 @@ def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
             ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
             *common, _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)), *tail,
             _ptr(z, "z", (M, D), False), _ptr(h0, "h0", (batch, D, N), False),
-            _ptr(y, "y", (M, D)), _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+            _ptr(y, "y", (M, D)), _ptr(hc, "h_cache", (batch, Lc, D, N), False),
             _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
         return y, hc, hl
     pu, lu = _rows(u, "u", M, D)
@@ -267,22 +277,25 @@ def selective_scan(u, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
     _check("mss_selective_scan_strided", lib().mss_selective_scan_strided(
         ctypes.byref(dims), ctypes.byref(st), _disc(disc), pu, pd, *common, pb, pc, *tail, pz,
         _ptr(h0, "h0", (batch, D, N), False), py,
-        _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+        _ptr(hc, "h_cache", (batch, Lc, D, N), False),
         _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
     return y, hc, hl
 
 
 def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=None, *, batch,
-                seq_len, disc, h_cache=False, h_last=False, out=None, stream=None, exact=False):
+                seq_len, disc, h_cache=False, h_last=False, out=None, stream=None, exact=False,
+                ckpt8=False):
     """Fused conv1d + SiLU + selective scan + gate from x.  Returns (y, h_cache, h_last).
 
     x, delta, z, B, C and ``out`` may be row-strided views (column slices).
-    ``exact``: no time split (the plain sequential recurrence, less parallel)."""
+    ``exact``: no time split (the plain sequential recurrence, less parallel).
+    ``ckpt8``: h_cache is the state entering every 8th step (see selective_scan)."""
     D, N = A_log.shape
     K = w_conv.shape[1]
     M = batch * seq_len
-    y, hc, hl = _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last)
-    dims = make_dims(batch, seq_len, D, N, K, exact)
+    Lc = ckpt_steps(seq_len) if ckpt8 else seq_len
+    y, hc, hl = _scan_outputs(x, batch, seq_len, D, N, out, h_cache, h_last, ckpt8)
+    dims = make_dims(batch, seq_len, D, N, K, exact, ckpt8)
     conv = (_ptr(w_conv, "w_conv", (D, K)), _ptr(b_conv, "b_conv", (D,), False))
     if _dense(x, delta, B, C, z, y):
         _check("mss_mamba1_core", lib().mss_mamba1_core(
@@ -290,7 +303,7 @@ def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=No
             _ptr(delta, "delta", (M, D)), _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)),
             _ptr(C, "C", (M, N)), _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
             _ptr(h0, "h0", (batch, D, N), False), _ptr(y, "y", (M, D)),
-            _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+            _ptr(hc, "h_cache", (batch, Lc, D, N), False),
             _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
         return y, hc, hl
     px, lx = _rows(x, "x", M, D)
@@ -304,7 +317,7 @@ def mamba1_core(x, w_conv, b_conv, delta, A_log, B, C, D_vec=None, z=None, h0=No
         ctypes.byref(dims), ctypes.byref(st), _disc(disc), px, *conv, pd,
         _ptr(A_log, "A_log", (D, N)), pb, pc, _ptr(D_vec, "D_vec", (D,), False), pz,
         _ptr(h0, "h0", (batch, D, N), False), py,
-        _ptr(hc, "h_cache", (batch, seq_len, D, N), False),
+        _ptr(hc, "h_cache", (batch, Lc, D, N), False),
         _ptr(hl, "h_last", (batch, D, N), False), _stream(stream)))
     return y, hc, hl
 
@@ -328,9 +341,11 @@ def selective_step(x, z, delta, A_log, B, C, D_vec, w_conv, b_conv, conv_state, 
     return y
 
 
-def workspace_bytes(op, *, batch, seq_len, d_inner, d_state, d_conv=1, exact=False) -> int:
-    """Workspace bytes a backward entry point needs (``op``: OP_* constant)."""
-    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv, exact)
+def workspace_bytes(op, *, batch, seq_len, d_inner, d_state, d_conv=1, exact=False,
+                    ckpt8=False) -> int:
+    """Workspace bytes a backward entry point needs (``op``: OP_* constant;
+    ``ckpt8``: the scan backward is given the forward's checkpoints)."""
+    dims = make_dims(batch, seq_len, d_inner, d_state, d_conv, exact, ckpt8)
     n = ctypes.c_size_t(0)
     _check("mss_workspace_bytes", lib().mss_workspace_bytes(ctypes.byref(dims), op,
                                                              ctypes.byref(n)))
@@ -377,7 +392,8 @@ def ssd_time_split(*, batch, seq_len, n_heads, head_dim, d_state, n_groups=1,
 
 
 def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch, seq_len, disc,
-                            need_dh0=False, workspace=None, stream=None, exact=False):
+                            need_dh0=False, workspace=None, stream=None, exact=False,
+                            h_ckpt=None):
     """Gradients of ``selective_scan``'s output against ``dout`` (batch*seq_len, D).
 
     Returns a dict: du, ddelta (M, D); dA_log (D, N); dB, dC (M, N);
@@ -385,6 +401,8 @@ def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
     dh0 (batch, D, N) when ``need_dh0``.  ``workspace``: optional uint8 GPU
     tensor of at least ``workspace_bytes(OP_SELECTIVE_SCAN_BACKWARD, ...)``
     + 256 bytes (allocated here when omitted).  ``exact``: no time split.
+    ``h_ckpt``: the forward's 8-step checkpoints (``h_cache`` of a forward
+    call with ``ckpt8=True``), from which every 8-step block starts.
     """
     D, N = A_log.shape
     M = batch * seq_len
@@ -393,14 +411,17 @@ def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
          "dD": _empty((D,), u) if D_vec is not None else None,
          "dz": _empty((M, D), u) if z is not None else None,
          "dh0": _empty((batch, D, N), u) if need_dh0 else None}
+    ck = h_ckpt is not None
     wp, wn, _keep = _workspace(OP_SELECTIVE_SCAN_BACKWARD, u, workspace, stream, batch=batch,
-                               seq_len=seq_len, d_inner=D, d_state=N, exact=exact)
-    dims = make_dims(batch, seq_len, D, N, 1, exact)
+                               seq_len=seq_len, d_inner=D, d_state=N, exact=exact, ckpt8=ck)
+    dims = make_dims(batch, seq_len, D, N, 1, exact, ck)
     _check("mss_selective_scan_backward", lib().mss_selective_scan_backward(
         ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
         _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
         _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
-        _ptr(h0, "h0", (batch, D, N), False), _ptr(dout, "dout", (M, D)),
+        _ptr(h0, "h0", (batch, D, N), False),
+        _ptr(h_ckpt, "h_ckpt", (batch, ckpt_steps(seq_len), D, N), False),
+        _ptr(dout, "dout", (M, D)),
         _ptr(g["du"], "du", (M, D)), _ptr(g["ddelta"], "ddelta", (M, D)),
         _ptr(g["dA_log"], "dA_log", (D, N)), _ptr(g["dB"], "dB", (M, N)),
         _ptr(g["dC"], "dC", (M, N)), _ptr(g["dD"], "dD", (D,), False),
@@ -411,7 +432,7 @@ def selective_scan_backward(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
 
 def selective_scan_backward_noalloc(u, delta, A_log, B, C, D_vec, z, h0, dout, *, batch,
                                     seq_len, disc, need_dh0=False, out=None, stream=None,
-                                    exact=False):
+                                    exact=False, h_ckpt=None):
     """``selective_scan_backward`` through the entry point whose workspace is the
     library's static scratch array (for callers that cannot allocate; at most
     NOALLOC_SCRATCH_BYTES of workspace; calls overlapping on one GPU race).
@@ -425,12 +446,14 @@ def selective_scan_backward_noalloc(u, delta, A_log, B, C, D_vec, z, h0, dout, *
             "dD": D_vec is not None, "dz": z is not None, "dh0": need_dh0}
     out = dict(out or {})
     g = {k: (out[k] if k in out else _empty(shapes[k], u)) if want[k] else None for k in shapes}
-    dims = make_dims(batch, seq_len, D, N, 1, exact)
+    dims = make_dims(batch, seq_len, D, N, 1, exact, h_ckpt is not None)
     _check("mss_selective_scan_backward_noalloc", lib().mss_selective_scan_backward_noalloc(
         ctypes.byref(dims), _disc(disc), _ptr(u, "u", (M, D)), _ptr(delta, "delta", (M, D)),
         _ptr(A_log, "A_log", (D, N)), _ptr(B, "B", (M, N)), _ptr(C, "C", (M, N)),
         _ptr(D_vec, "D_vec", (D,), False), _ptr(z, "z", (M, D), False),
-        _ptr(h0, "h0", (batch, D, N), False), _ptr(dout, "dout", (M, D)),
+        _ptr(h0, "h0", (batch, D, N), False),
+        _ptr(h_ckpt, "h_ckpt", (batch, ckpt_steps(seq_len), D, N), False),
+        _ptr(dout, "dout", (M, D)),
         _ptr(g["du"], "du", (M, D)), _ptr(g["ddelta"], "ddelta", (M, D)),
         _ptr(g["dA_log"], "dA_log", (D, N)), _ptr(g["dB"], "dB", (M, N)),
         _ptr(g["dC"], "dC", (M, N)), _ptr(g["dD"], "dD", (D,), False),

@@ -10,10 +10,11 @@
 namespace mss {
 
 // Work split of a scan launch: the flattened (column tile, t) space of
-// `total = B * tiles_per_b * L` steps is cut into segments of `seg` steps,
+// `total = B * tiles_per_b * Lp` steps (each tile padded to Lp = L rounded up
+// to a multiple of 8) is cut into segments of `seg` steps (a multiple of 8),
 // one wave64 each.
 struct ScanShape {
-    int64_t B, L, D;
+    int64_t B, L, Lp, D;
     int N, K;
     int64_t tiles_per_b;
     int64_t total;
@@ -22,6 +23,7 @@ struct ScanShape {
     int64_t ld_src, ld_z, ld_delta, ld_B, ld_C, ld_y;
     bool bc_vec;              // B and C rows 16-byte aligned: staged block loads
     bool dense;               // strides are exactly D (activations) and N (B, C)
+    bool ckpt8;               // h_cache holds the state entering every 8th step
 };
 
 struct ScanArgs {

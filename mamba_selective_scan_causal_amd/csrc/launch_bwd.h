@@ -10,18 +10,21 @@
 namespace mss {
 
 // Backward of the scan: the flattened (tile, t) space of the B * tiles_per_b
-// channel tiles (batch row, 32 channels) is cut into `waves` segments of
-// `seg` steps, one wave each; a segment crossing the end of a tile is worked
-// as one piece per tile, and a tile has at most `pieces` pieces.  Workspace
-// regions (all fp32):
+// channel tiles (batch row, 32 channels), each tile padded to Lp = L rounded
+// up to a multiple of 8 steps, is cut into `waves` segments of `seg` steps
+// (a multiple of 8), one wave each; so every piece starts at a multiple of
+// 8.  A segment crossing the end of a tile is worked as one piece per tile
+// (the padding steps are skipped), and a tile has at most `pieces` pieces.
+// Workspace regions (all fp32):
 //   ckpt  (waves, blocks_per_seg, 64, 8)   h at every 8-step block start
+//                                          (absent when the forward's checkpoints are given)
 //   partB, partC (B, tiles_per_b, L, 16)    per-tile dB / dC rows
 //   partA (tiles, pieces, 64, 8), partD (tiles, pieces, 32)  per-piece dA / dD sums
 struct BwdShape {
-    int64_t B, L, D;
+    int64_t B, L, Lp, D;
     int N;
     int64_t tiles_per_b;      // ceil(D / 32)
-    int64_t total;            // B * tiles_per_b * L
+    int64_t total;            // B * tiles_per_b * Lp
     int64_t seg, waves, blocks_per_seg, pieces;
     bool bc_vec;              // B and C rows 16-byte aligned (N = 16)
 };
@@ -36,6 +39,7 @@ struct BwdArgs {
     const float* D_vec;
     const float* z;
     const float* h0;
+    const float* h_ckpt;      // (B, ceil(L/8), D, N): the forward's state entering steps 0, 8, ... or null
     const float* dout;
     float* du;
     float* ddelta;

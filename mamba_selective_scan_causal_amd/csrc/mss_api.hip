@@ -23,7 +23,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int32_t kKnownFlags = MSS_FLAG_EXACT;   // every other flag bit is rejected
+constexpr int32_t kKnownFlags = MSS_FLAG_EXACT | MSS_FLAG_CKPT8;   // every other bit is rejected
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = static_cast<int>(e);
@@ -147,6 +147,7 @@ int check_dims(const mss_dims* dims, bool need_l, bool need_k) {
 #endif
 
 bool exact(const mss_dims* dims) { return (dims->flags & MSS_FLAG_EXACT) != 0; }
+bool ckpt8(const mss_dims* dims) { return (dims->flags & MSS_FLAG_CKPT8) != 0; }
 
 // Segment length (steps of the flattened (tile, t) space) for `total` steps
 // over tiles of L steps: equal segments for about `target` waves, none
@@ -167,8 +168,9 @@ mss::ScanShape scan_shape(const mss_dims* dims, const mss_strides& ld, const flo
     s.N = static_cast<int>(dims->d_state);
     s.K = static_cast<int>(dims->d_conv);
     s.tiles_per_b = (s.D + 63) / 64;
-    s.total = s.B * s.tiles_per_b * s.L;
-    s.seg = split(s.total, s.L, MSS_SCAN_TARGET_WAVES, MSS_SCAN_MIN_SEG, exact(dims));
+    s.Lp = (s.L + 7) / 8 * 8;
+    s.total = s.B * s.tiles_per_b * s.Lp;
+    s.seg = (split(s.total, s.Lp, MSS_SCAN_TARGET_WAVES, MSS_SCAN_MIN_SEG, exact(dims)) + 7) / 8 * 8;
     s.ld_src = ld.x;
     s.ld_z = ld.z;
     s.ld_delta = ld.delta;
@@ -209,9 +211,12 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
     const int64_t Bt = dims->batch, L = dims->seq_len, D = dims->d_inner, N = dims->d_state;
     const int64_t K = dims->d_conv;
     int64_t M, MD, MN, DN, DK, BDN, BLDN;
+    // h_cache: every step's state, or (MSS_FLAG_CKPT8) the state entering
+    // every 8th step
+    const int64_t Lc = ckpt8(dims) ? (L + 7) / 8 : L;
     if (!count(M, {Bt, L}) || !count(MD, {Bt, L, D}) || !count(MN, {Bt, L, N}) ||
         !count(DN, {D, N}) || !count(DK, {D, K}) || !count(BDN, {Bt, D, N}) ||
-        (h_cache && !count(BLDN, {Bt, L, D, N})))
+        (h_cache && !count(BLDN, {Bt, Lc, D, N})))
         return MSS_EINVAL;
     if (!h_cache) BLDN = 0;
     Checker ck;
@@ -249,7 +254,9 @@ int scan_common(const mss_dims* dims, const mss_strides* strides, bool strided, 
     }
     const mss::ScanArgs a{disc, fused, src, delta, A_log, B, C, D_vec, z, h0, w_conv, b_conv,
                           y, h_cache, h_last};
-    const hipError_t e = mss::launch_scan(a, scan_shape(dims, ld, B, C, z), stream);
+    mss::ScanShape sh = scan_shape(dims, ld, B, C, z);
+    sh.ckpt8 = ckpt8(dims);
+    const hipError_t e = mss::launch_scan(a, sh, stream);
     return e == hipSuccess ? MSS_OK : hip_fail(e);
 }
 
@@ -271,13 +278,15 @@ mss::BwdShape bwd_shape(const mss_dims* dims) {
     s.D = dims->d_inner;
     s.N = static_cast<int>(dims->d_state);
     s.tiles_per_b = (s.D + kBwdTile - 1) / kBwdTile;
-    s.total = s.B * s.tiles_per_b * s.L;   // fits: B L D was counted without overflow
-    const int64_t seg = split(s.total, s.L, MSS_BWD_TARGET_WAVES, MSS_BWD_MIN_SEG, exact(dims));
+    s.Lp = align_up(s.L, kBwdBlock);
+    s.total = s.B * s.tiles_per_b * s.Lp;   // fits: B L D was counted without overflow
+    const int64_t seg =
+        align_up(split(s.total, s.Lp, MSS_BWD_TARGET_WAVES, MSS_BWD_MIN_SEG, exact(dims)), kBwdBlock);
     s.seg = seg;
     s.waves = (s.total + seg - 1) / seg;
     s.blocks_per_seg = (seg + kBwdBlock - 1) / kBwdBlock;
-    // a tile of L steps meets at most ceil(L / seg) + 1 segments
-    s.pieces = (s.L + seg - 1) / seg + 1;
+    // a tile of Lp steps meets at most ceil(Lp / seg) + 1 segments
+    s.pieces = (s.Lp + seg - 1) / seg + 1;
     s.bc_vec = false;
     return s;
 }
@@ -287,9 +296,11 @@ struct BwdLayout {
     int64_t ckpt, partB, partC, partA, partD, total;
 };
 
-bool bwd_layout(const mss::BwdShape& s, BwdLayout& o) {
+// with_ckpt false: the forward's checkpoints are given and the checkpoint
+// region is not needed.
+bool bwd_layout(const mss::BwdShape& s, BwdLayout& o, bool with_ckpt) {
     int64_t ck, pb, pa, pd;
-    if (!count(ck, {s.waves, s.blocks_per_seg, 64 * 8 * 4}) ||
+    if (!count(ck, {with_ckpt ? s.waves : 0, s.blocks_per_seg, 64 * 8 * 4}) ||
         !count(pb, {s.B, s.tiles_per_b, s.L, 16 * 4}) ||
         !count(pa, {s.B, s.tiles_per_b, s.pieces, 64 * 8 * 4}) ||
         !count(pd, {s.B, s.tiles_per_b, s.pieces, 32 * 4}))
@@ -397,7 +408,7 @@ int scratch_address(void** out) {
 // then ignored).
 int scan_bwd_common(const mss_dims* dims, int disc, const float* u, const float* delta,
                     const float* A_log, const float* B, const float* C, const float* D_vec,
-                    const float* z, const float* h0, const float* dout, float* du,
+                    const float* z, const float* h0, const float* h_ckpt, const float* dout, float* du,
                     float* ddelta, float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
                     float* dh0, bool use_scratch, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
@@ -410,8 +421,14 @@ int scan_bwd_common(const mss_dims* dims, int disc, const float* u, const float*
         !count(BDN, {Bt, D, N}))
         return MSS_EINVAL;
     if (z && !dz && MD > 0) return MSS_EINVAL;
+    // MSS_FLAG_CKPT8 and h_ckpt go together (the flag sizes the workspace)
+    const bool with_ck = ckpt8(dims);
+    if (with_ck != (h_ckpt != nullptr) && MD > 0) return MSS_EINVAL;
+    int64_t BKDN = 0;
+    if (with_ck && !count(BKDN, {Bt, (L + 7) / 8, D, N})) return MSS_EINVAL;
     Checker ck;
     ck.in(u, MD, true);
+    ck.in(h_ckpt, BKDN, false);
     ck.in(delta, MD, true);
     ck.in(A_log, DN, true);
     ck.in(B, MN, true);
@@ -433,7 +450,7 @@ int scan_bwd_common(const mss_dims* dims, int disc, const float* u, const float*
     BwdLayout lay{};
     if (MD > 0) {
         s = bwd_shape(dims);
-        if (!bwd_layout(s, lay)) return MSS_EINVAL;
+        if (!bwd_layout(s, lay, !with_ck)) return MSS_EINVAL;
         if (s.waves > INT32_MAX) return MSS_EINVAL;   // grid size
         need = lay.total;
     }
@@ -463,7 +480,8 @@ int scan_bwd_common(const mss_dims* dims, int disc, const float* u, const float*
     s.bc_vec = N == 16 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
                reinterpret_cast<uintptr_t>(C) % 16 == 0;
     char* w = static_cast<char*>(workspace);
-    const mss::BwdArgs a{disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta, dA_log,
+    const mss::BwdArgs a{disc, u, delta, A_log, B, C, D_vec, z, h0, with_ck ? h_ckpt : nullptr,
+                         dout, du, ddelta, dA_log,
                          dB, dC, dD_vec, z ? dz : nullptr, dh0,
                          reinterpret_cast<float*>(w + lay.ckpt),
                          reinterpret_cast<float*>(w + lay.partB),
@@ -522,7 +540,7 @@ int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes) {
         if (!count(MD, {dims->batch, dims->seq_len, dims->d_inner})) return MSS_EINVAL;
         if (MD == 0) return MSS_OK;
         BwdLayout lay;
-        if (!bwd_layout(bwd_shape(dims), lay)) return MSS_EINVAL;
+        if (!bwd_layout(bwd_shape(dims), lay, !ckpt8(dims))) return MSS_EINVAL;
         *bytes = static_cast<size_t>(lay.total);
         return MSS_OK;
     }
@@ -541,11 +559,11 @@ int mss_workspace_bytes(const mss_dims* dims, int op, size_t* bytes) {
 int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
                                 const float* delta, const float* A_log, const float* B,
                                 const float* C, const float* D_vec, const float* z,
-                                const float* h0, const float* dout, float* du, float* ddelta,
-                                float* dA_log, float* dB, float* dC, float* dD_vec, float* dz,
-                                float* dh0, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
-    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta,
+                                const float* h0, const float* h_ckpt, const float* dout,
+                                float* du, float* ddelta, float* dA_log, float* dB, float* dC,
+                                float* dD_vec, float* dz, float* dh0, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, h_ckpt, dout, du, ddelta,
                            dA_log, dB, dC, dD_vec, dz, dh0, false, workspace, workspace_bytes,
                            stream);
 }
@@ -553,11 +571,11 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
 int mss_selective_scan_backward_noalloc(const mss_dims* dims, int disc, const float* u,
                                         const float* delta, const float* A_log, const float* B,
                                         const float* C, const float* D_vec, const float* z,
-                                        const float* h0, const float* dout, float* du,
-                                        float* ddelta, float* dA_log, float* dB, float* dC,
-                                        float* dD_vec, float* dz, float* dh0,
+                                        const float* h0, const float* h_ckpt, const float* dout,
+                                        float* du, float* ddelta, float* dA_log, float* dB,
+                                        float* dC, float* dD_vec, float* dz, float* dh0,
                                         hipStream_t stream) {
-    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, dout, du, ddelta,
+    return scan_bwd_common(dims, disc, u, delta, A_log, B, C, D_vec, z, h0, h_ckpt, dout, du, ddelta,
                            dA_log, dB, dC, dD_vec, dz, dh0, true, nullptr, 0, stream);
 }
 

@@ -24,6 +24,8 @@
 //   1. h(t0-1) by decay-bounded forward replay (as in the forward kernel).
 //   2. Forward over the segment, storing h at every 8-step block start in the
 //      checkpoint workspace (2 KB per block).
+//   (1 and 2 are skipped when the forward pass's own states at every 8th
+//   step are given: the blocks then start from those.)
 //   3. The adjoint carried into t1-1 by decay-bounded reverse replay: walk
 //      delta forward from t1 until every lane's slowest state has decayed by
 //      2^-c (c = MSS_REPLAY_DECAY_BITS), then run the adjoint recurrence
@@ -61,6 +63,7 @@ struct BwdCols {
     const float* __restrict__ Dv;
     const float* __restrict__ z;
     const float* __restrict__ h0;
+    const float* __restrict__ hck;    // (B, ceil(L/8), D, N) or null
     const float* __restrict__ dout;
     float* __restrict__ du;
     float* __restrict__ ddelta;
@@ -641,18 +644,26 @@ __device__ __forceinline__ void bwd_piece(const BwdCols& c, const BwdShape& s, i
     Bwd<DISC, NS> bw(c, s, b, ct * 32 + (lane & 31u), lds);
     bw.init();
 
-    // 1. h(t0 - 1)
-    float h[kH];
-    const int64_t tw = bw.replay_start(t0);
+    if (!c.hck) {
+        // 1. h(t0 - 1)
+        float h[kH];
+        const int64_t tw = bw.replay_start(t0);
 #pragma unroll
-    for (int j = 0; j < kH; j++)
-        h[j] = (tw == 0 && c.h0 && bw.valid(j)) ? c.h0[(b * s.D + bw.d) * bw.N + bw.half * kH + j] : 0.0f;
-    bw.template fwd_sweep<false>(h, tw, t0, nullptr);
+        for (int j = 0; j < kH; j++)
+            h[j] = (tw == 0 && c.h0 && bw.valid(j))
+                       ? c.h0[(b * s.D + bw.d) * bw.N + bw.half * kH + j]
+                       : 0.0f;
+        bw.template fwd_sweep<false>(h, tw, t0, nullptr);
 
-    // 2. checkpoints of the piece
-    bw.template fwd_sweep<true>(h, t0, t1, ck);
-    // The checkpoints are read back by this wave below.
-    __threadfence_block();
+        // 2. checkpoints of the piece
+        bw.template fwd_sweep<true>(h, t0, t1, ck);
+        // The checkpoints are read back by this wave below.
+        __threadfence_block();
+    }
+    // (with the forward's checkpoints, every block below starts from them:
+    // t0 is a multiple of 8, so the blocks of the piece are the 8-step
+    // blocks of the checkpoints)
+    const int64_t nck = (s.L + 7) >> 3;
 
     // 3. adjoint carried into t1 - 1
     float g[kH];
@@ -680,9 +691,26 @@ __device__ __forceinline__ void bwd_piece(const BwdCols& c, const BwdShape& s, i
             go[i] = bw.ld(c.dout, t);
             zz[i] = c.z ? bw.ld(c.z, t) : 0.0f;
         }
-        const float4* p = reinterpret_cast<const float4*>(ck + k * (kWave * kH)) + lane;
-        const float4 h_lo = p[0], h_hi = p[kWave];
-        const float hin[kH] = {h_lo.x, h_lo.y, h_lo.z, h_lo.w, h_hi.x, h_hi.y, h_hi.z, h_hi.w};
+        float hin[kH];
+        if (c.hck) {
+            // this lane's 8 states of the block's start: a channel's 16
+            // states are 64 contiguous bytes, the tile's 32 channels 2 KB
+            const float* p = c.hck + ((b * nck + (st >> 3)) * s.D + bw.d) * bw.N + bw.half * kH;
+            if constexpr (NS == 16) {
+                const float4 lo = reinterpret_cast<const float4*>(p)[0];
+                const float4 hi = reinterpret_cast<const float4*>(p)[1];
+                hin[0] = lo.x; hin[1] = lo.y; hin[2] = lo.z; hin[3] = lo.w;
+                hin[4] = hi.x; hin[5] = hi.y; hin[6] = hi.z; hin[7] = hi.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < kH; j++) hin[j] = bw.valid(j) ? p[j] : 0.0f;
+            }
+        } else {
+            const float4* p = reinterpret_cast<const float4*>(ck + k * (kWave * kH)) + lane;
+            const float4 h_lo = p[0], h_hi = p[kWave];
+            hin[0] = h_lo.x; hin[1] = h_lo.y; hin[2] = h_lo.z; hin[3] = h_lo.w;
+            hin[4] = h_hi.x; hin[5] = h_hi.y; hin[6] = h_hi.z; hin[7] = h_hi.w;
+        }
         bw.stage(st);
 #pragma unroll
         for (int i = 0; i < kT; i++) dv[i] = softplus(dl[i]);
@@ -720,10 +748,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int64_t g1 = g0 + s.seg < s.total ? g0 + s.seg : s.total;
     float* ck = c.ckpt + w * s.blocks_per_seg * (kWave * kH);
     for (int64_t g = g0; g < g1;) {
-        const int64_t ti = g / s.L;
-        const int64_t t0 = g - ti * s.L;
+        const int64_t ti = g / s.Lp;
+        const int64_t t0 = g - ti * s.Lp;
+        if (t0 >= s.L) {        // the tile's padding steps
+            g = (ti + 1) * s.Lp;
+            continue;
+        }
         const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
-        const int64_t slot = w - (ti * s.L) / s.seg;   // waves before w that cover tile ti
+        const int64_t slot = w - (ti * s.Lp) / s.seg;   // waves before w that cover tile ti
         bwd_piece<DISC, NS>(c, s, ti, t0, t1, slot, ck, lds);
         g += t1 - t0;
     }
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
 // Number of pieces of tile ti (one per wave whose step range meets it).
 __device__ __forceinline__ int64_t tile_pieces(const BwdShape& s, int64_t ti) {
-    return (ti * s.L + s.L - 1) / s.seg - (ti * s.L) / s.seg + 1;
+    return (ti * s.Lp + s.L - 1) / s.seg - (ti * s.Lp) / s.seg + 1;
 }
 
 // Cross-tile and cross-piece sums, fixed order:
@@ -811,8 +843,9 @@ hipError_t launch_t(const BwdCols& c, const BwdShape& s, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_scan_bwd(const BwdArgs& a, const BwdShape& s, hipStream_t st) {
-    BwdCols c{a.u,  a.delta,  a.A_log, a.B,    a.C,     a.D_vec, a.z,     a.h0,    a.dout,
-              a.du, a.ddelta, a.dz,    a.dh0,  a.ckpt,  a.partB, a.partC, a.partA, a.partD};
+    BwdCols c{a.u,     a.delta, a.A_log, a.B,     a.C,     a.D_vec, a.z,
+              a.h0,    a.h_ckpt, a.dout, a.du,    a.ddelta, a.dz,   a.dh0,
+              a.ckpt,  a.partB, a.partC, a.partA, a.partD};
     hipError_t e;
     const bool vec = s.N == 16 && s.bc_vec;
     if (a.disc == MSS_DISC_EULER)

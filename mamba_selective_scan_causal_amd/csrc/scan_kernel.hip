@@ -78,12 +78,19 @@ struct Lane {
 constexpr int kWarm = 0;     // state only
 constexpr int kOut = 1;      // y
 constexpr int kOutHC = 2;    // y and hCache
+constexpr int kOutCK = 3;    // y and the state entering every 8th step
+
+// State-cache modes of a kernel instantiation.
+constexpr int kCacheNone = 0;
+constexpr int kCacheAll = 1;     // h_cache (B, L, D, N): every step's state
+constexpr int kCacheCk8 = 2;     // h_cache (B, ceil(L/8), D, N): the state entering steps 0, 8, 16, ...
 
 // DN: every activation row stride is D and the B/C stride is N (dense
 // tensors); the strides then fold into one row offset per step.
-// HC: the hCache mode (a kernel of its own, so that the staging of the state
-// cache does not take registers from the kernel without it).
-template <int DISC, int KS, int NS, bool DN, bool HC>
+// CM: the state-cache mode (kCache*; each a kernel of its own, so that the
+// staging of the state cache does not take registers from the kernel
+// without it).
+template <int DISC, int KS, int NS, bool DN, int CM>
 struct Scan {
     using L_t = Lane<KS, NS>;
     static constexpr int NR = L_t::NR;
@@ -207,6 +214,39 @@ struct Scan {
         }
     }
 
+    // This wave's states, stored to the state-cache row `hc` ((D, N) of one
+    // step).
+    __device__ __forceinline__ void store_state(const L_t& ln, float* __restrict__ hc) const {
+        if constexpr (NS == 16) {
+            // The wave's 64 x 16 states of the step are one contiguous
+            // 4 KB block: through LDS (80-byte lane stride, conflict
+            // free) so that each 16-byte store instruction writes 1 KB
+            // contiguously (a lane storing its own 64 bytes would
+            // spread every store over 4 KB).  One wave per workgroup:
+            // its LDS accesses complete in program order.
+            const uint32_t lane = threadIdx.x;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                hst[5 * lane + j] = make_float4(ln.h[4 * j], ln.h[4 * j + 1],
+                                                ln.h[4 * j + 2], ln.h[4 * j + 3]);
+            float4* hb = reinterpret_cast<float4*>(hc + d0 * 16);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int q = i * kWave + static_cast<int>(lane);
+                if (d0 + q / 4 < D) hb[q] = hst[5 * (q / 4) + (q % 4)];
+            }
+        } else if constexpr (NS > 0 && NS % 4 == 0) {
+#pragma unroll
+            for (int n = 0; n < NR; n += 4)
+                *reinterpret_cast<float4*>(hc + d * NS + n) =
+                    make_float4(ln.h[n], ln.h[n + 1], ln.h[n + 2], ln.h[n + 3]);
+        } else {
+#pragma unroll
+            for (int n = 0; n < NR; n++)
+                if (n < N) hc[d * N + n] = ln.h[n];
+        }
+    }
+
     // One time step.  SLOW: some lane has |dv A| < 2^-6 (see below).
     // LDS: B_t / C_t come from the staged block at row i; otherwise from
     // scalar loads.
@@ -295,35 +335,11 @@ struct Scan {
             const float g = silu(zv);
             (c.y + r * ldy)[d] = gated ? yv * g : yv;
             if constexpr (OUT == kOutHC) {
-                float* __restrict__ hc = c.h_cache + r * D * N;
-                if constexpr (NS == 16) {
-                    // The wave's 64 x 16 states of the step are one contiguous
-                    // 4 KB block: through LDS (80-byte lane stride, conflict
-                    // free) so that each 16-byte store instruction writes 1 KB
-                    // contiguously (a lane storing its own 64 bytes would
-                    // spread every store over 4 KB).  One wave per workgroup:
-                    // its LDS accesses complete in program order.
-                    const uint32_t lane = threadIdx.x;
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        hst[5 * lane + j] = make_float4(ln.h[4 * j], ln.h[4 * j + 1],
-                                                        ln.h[4 * j + 2], ln.h[4 * j + 3]);
-                    float4* hb = reinterpret_cast<float4*>(hc + d0 * 16);
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int q = i * kWave + static_cast<int>(lane);
-                        if (d0 + q / 4 < D) hb[q] = hst[5 * (q / 4) + (q % 4)];
-                    }
-                } else if constexpr (NS > 0 && NS % 4 == 0) {
-#pragma unroll
-                    for (int n = 0; n < NR; n += 4)
-                        *reinterpret_cast<float4*>(hc + d * NS + n) =
-                            make_float4(ln.h[n], ln.h[n + 1], ln.h[n + 2], ln.h[n + 3]);
-                } else {
-#pragma unroll
-                    for (int n = 0; n < NR; n++)
-                        if (n < N) hc[d * N + n] = ln.h[n];
-                }
+                store_state(ln, c.h_cache + r * D * N);
+            } else if constexpr (OUT == kOutCK) {
+                // the state entering step t + 1, when that is a multiple of 8
+                if (((t + 1) & 7) == 0 && t + 1 < L)
+                    store_state(ln, c.h_cache + (b * ((L + 7) >> 3) + ((t + 1) >> 3)) * D * N);
             }
         }
     }
@@ -381,8 +397,15 @@ struct Scan {
                 // ~3e-8 next to 1) then compounds over at most ~64 steps of
                 // memory, and a single step with tiny dv A adds one such error.
                 if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {
+                    // (checkpoints fall on block ends -- segments start at
+                    // multiples of 8 -- so the straight-line block has no
+                    // branch in it and the checkpoint follows it)
+                    constexpr int OB = OUT == kOutCK ? kOut : OUT;
 #pragma unroll
-                    for (int i = 0; i < kT; i++) step<OUT, false, true>(ln, cx[i], dv[i], cz[i], t + i, i);
+                    for (int i = 0; i < kT; i++) step<OB, false, true>(ln, cx[i], dv[i], cz[i], t + i, i);
+                    if constexpr (OUT == kOutCK)
+                        if (t + kT < L)
+                            store_state(ln, c.h_cache + (b * ((L + 7) >> 3) + ((t + kT) >> 3)) * D * N);
                 } else {
                     steps1<OUT, true>(ln, t, kT);
                 }
@@ -577,10 +600,14 @@ struct Scan {
                 if (NS > 0 || n < N) ln.h[n] = c.h0[(b * D + d) * N + n];
         }
         load_window(ln, t0);
-        if constexpr (HC)
+        if constexpr (CM == kCacheAll) {
             sweep<kOutHC>(ln, t0, t1);
-        else
+        } else if constexpr (CM == kCacheCk8) {
+            if (t0 == 0) store_state(ln, c.h_cache + b * ((L + 7) >> 3) * D * N);
+            sweep<kOutCK>(ln, t0, t1);
+        } else {
             sweep<kOut>(ln, t0, t1);
+        }
         if (t1 == L && c.h_last) {
 #pragma unroll
             for (int n = 0; n < NR; n++)
@@ -591,23 +618,29 @@ struct Scan {
 
 // Two waves per SIMD: one wave alone issues VALU work only about every other
 // slot, so the register budget is capped at 256 VGPRs.
-template <int DISC, int KS, int NS, bool DN, bool HC>
+template <int DISC, int KS, int NS, bool DN, int CM>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_kernel(
     Cols c, ScanShape s) {
     __shared__ float4 lds[kWave];
-    __shared__ float4 hst[NS == 16 && HC ? 5 * kWave : 1];
+    __shared__ float4 hst[NS == 16 && CM != kCacheNone ? 5 * kWave : 1];
     const int64_t lane = threadIdx.x;
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * s.seg;
     const int64_t g1 = g0 + s.seg < s.total ? g0 + s.seg : s.total;
     // A segment of the flattened (tile, t) space may cover the end of one
-    // tile and the start of the next; walk its pieces.
+    // tile and the start of the next; walk its pieces.  Tiles are padded to
+    // Lp steps (a multiple of 8) and segments are multiples of 8 long, so
+    // every piece starts at a multiple of 8; the padding is skipped.
     for (int64_t g = g0; g < g1;) {
-        const int64_t tile = g / s.L;
-        const int64_t t0 = g - tile * s.L;
+        const int64_t tile = g / s.Lp;
+        const int64_t t0 = g - tile * s.Lp;
+        if (t0 >= s.L) {
+            g = (tile + 1) * s.Lp;
+            continue;
+        }
         const int64_t t1 = t0 + (g1 - g) < s.L ? t0 + (g1 - g) : s.L;
         const int64_t b = tile / s.tiles_per_b;
         const int64_t dt = tile - b * s.tiles_per_b;
-        Scan<DISC, KS, NS, DN, HC> sc(c, s, b, dt * kWave + lane, lds, hst);
+        Scan<DISC, KS, NS, DN, CM> sc(c, s, b, dt * kWave + lane, lds, hst);
         sc.run(t0, t1);
         g += t1 - t0;
     }
@@ -616,12 +649,16 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 template <int DISC, int KS, int NS, bool DN>
 hipError_t launch_t(const Cols& c, const ScanShape& s, hipStream_t st) {
     const int64_t nblk = (s.total + s.seg - 1) / s.seg;
-    if (c.h_cache)
-        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, true>),
-                           dim3(static_cast<unsigned>(nblk)), dim3(kWave), 0, st, c, s);
+    const dim3 grid(static_cast<unsigned>(nblk));
+    if (c.h_cache && s.ckpt8)
+        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, kCacheCk8>), grid, dim3(kWave), 0, st, c,
+                           s);
+    else if (c.h_cache)
+        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, kCacheAll>), grid, dim3(kWave), 0, st, c,
+                           s);
     else
-        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, false>),
-                           dim3(static_cast<unsigned>(nblk)), dim3(kWave), 0, st, c, s);
+        hipLaunchKernelGGL((scan_kernel<DISC, KS, NS, DN, kCacheNone>), grid, dim3(kWave), 0, st,
+                           c, s);
     return hipGetLastError();
 }
 

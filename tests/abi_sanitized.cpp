@@ -74,9 +74,9 @@ int step(const mss_dims* d, float* x, float* h) {
 
 int scan_bwd(const mss_dims* d, float* du, void* ws, size_t ws_bytes) {
     return mss_selective_scan_backward(d, MSS_DISC_ZOH, fake(1), fake(2), fake(3), fake(4),
-                                       fake(5), nullptr, nullptr, nullptr, fake(6), du, fake(8),
-                                       fake(9), fake(10), fake(11), nullptr, nullptr, nullptr, ws,
-                                       ws_bytes, nullptr);
+                                       fake(5), nullptr, nullptr, nullptr, nullptr, fake(6), du,
+                                       fake(8), fake(9), fake(10), fake(11), nullptr, nullptr,
+                                       nullptr, ws, ws_bytes, nullptr);
 }
 
 int conv_bwd(const mss_dims* d, float* dx, void* ws, size_t ws_bytes) {
@@ -104,7 +104,7 @@ int main() {
     bad.struct_size = 8;
     expect(scan(&bad, 0, fake(1), fake(9)), MSS_EINVAL, "scan: struct_size");
     bad = d;
-    bad.flags = 2;
+    bad.flags = 4;
     expect(scan(&bad, 0, fake(1), fake(9)), MSS_EINVAL, "scan: unknown flag");
     mss_dims n17 = dims(2, 64, 128, 17, 4);
     expect(scan(&n17, 0, fake(1), fake(9)), MSS_EINVAL, "scan: N = 17");
@@ -175,6 +175,9 @@ int main() {
     expect(scan_bwd(&d, fake(7), misaligned(20), need), MSS_EALIGN, "scan bwd: workspace align");
     expect(scan_bwd(&d, fake(1), fake(20), need), MSS_EALIAS, "scan bwd: du aliases u");
     expect(scan_bwd(&d, fake(7), fake(1), need), MSS_EALIAS, "scan bwd: workspace aliases u");
+    mss_dims dck = d;
+    dck.flags = MSS_FLAG_CKPT8;   // checkpoints announced but not given
+    expect(scan_bwd(&dck, fake(7), fake(20), need), MSS_EINVAL, "scan bwd: CKPT8 without h_ckpt");
     size_t cneed = 0;
     expect(mss_workspace_bytes(&d, MSS_OP_CONV1D_SILU_BACKWARD, &cneed), MSS_OK, "conv ws query");
     expect(conv_bwd(&d, fake(1), fake(20), cneed), MSS_EALIAS, "conv bwd: dx aliases x");

@@ -44,8 +44,10 @@ def a2_of(A_log) -> np.ndarray:
 
 def segment_starts(tile: int, L: int, seg: int):
     """Steps t0 in (0, L) of `tile` at which a segment of the flattened
-    (tile, t) space starts (the split that mss_time_split reports)."""
-    first = (-tile * L) % seg
+    (tile, t) space starts (the split that mss_time_split reports: tiles
+    padded to a multiple of 8 steps)."""
+    Lp = (L + 7) // 8 * 8
+    first = (-tile * Lp) % seg
     return [t for t in range(first, L, seg) if t > 0]
 
 

@@ -70,7 +70,7 @@ def test_scan_validation(L):
     bad.struct_size = 40
     assert scan_call(L, bad) == EINVAL
     bad = mss.make_dims(2, 16, 64, 16, 4)
-    bad.flags = 2                                                         # unknown flag bit
+    bad.flags = 4                                                         # unknown flag bit
     assert scan_call(L, bad) == EINVAL
     bad.flags = -1
     assert scan_call(L, bad) == EINVAL
@@ -240,8 +240,9 @@ def test_workspace_query(L):
 
 def scan_bwd_call(L, dims, disc=0, ws_size=None, **over):
     args = dict(u=fake(1), delta=fake(2), A_log=fake(3), B=fake(4), C=fake(5), D_vec=fake(6),
-                z=fake(7), h0=None, dout=fake(8), du=fake(9), ddelta=fake(10), dA_log=fake(11),
-                dB=fake(12), dC=fake(13), dD=fake(14), dz=fake(15), dh0=None, ws=fake(16))
+                z=fake(7), h0=None, h_ckpt=None, dout=fake(8), du=fake(9), ddelta=fake(10),
+                dA_log=fake(11), dB=fake(12), dC=fake(13), dD=fake(14), dz=fake(15), dh0=None,
+                ws=fake(16))
     args.update(over)
     if ws_size is None:
         ws_size = ws_bytes(L, dims, OP_SCAN_BWD)[1]
@@ -263,6 +264,16 @@ def test_scan_backward_validation(L):
     need = ws_bytes(L, d, OP_SCAN_BWD)[1]
     assert scan_bwd_call(L, d, ws_size=need - 1) == EWORKSPACE
     assert scan_bwd_call(L, d, ws=ctypes.c_void_p(BASE + 16 * (1 << 32) + 16)) == EALIGN
+    # checkpoints from the forward: the flag and the pointer go together, the
+    # checkpoints are an input (no output may overlap them), and they shrink
+    # the workspace
+    dck = mss.make_dims(2, 64, 64, 16, 4, ckpt8=True)
+    need_ck = ws_bytes(L, dck, OP_SCAN_BWD)[1]
+    assert 0 < need_ck < need
+    assert scan_bwd_call(L, dck, ws_size=need_ck) == EINVAL              # flag without h_ckpt
+    assert scan_bwd_call(L, d, h_ckpt=fake(17)) == EINVAL                # h_ckpt without flag
+    assert scan_bwd_call(L, dck, h_ckpt=fake(17), ws_size=need_ck - 1) == EWORKSPACE
+    assert scan_bwd_call(L, dck, h_ckpt=fake(9), ws_size=need_ck) == EALIAS   # du on h_ckpt
 
 
 def conv_bwd_call(L, dims, ws_size=None, **over):
@@ -342,7 +353,7 @@ def test_noalloc_backward_refuses_past_its_scratch(L):
 
     def call(dims, disc=0, **over):
         args = dict(u=fake(1), delta=fake(2), A_log=fake(3), B=fake(4), C=fake(5),
-                    D_vec=fake(6), z=fake(7), h0=None, dout=fake(8), du=fake(9),
+                    D_vec=fake(6), z=fake(7), h0=None, h_ckpt=None, dout=fake(8), du=fake(9),
                     ddelta=fake(10), dA_log=fake(11), dB=fake(12), dC=fake(13), dD=fake(14),
                     dz=fake(15), dh0=None)
         args.update(over)

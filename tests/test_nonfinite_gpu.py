@@ -67,21 +67,25 @@ def test_core_contains_nonfinite_inputs(disc):
 @pytest.mark.parametrize("disc", DISCS)
 def test_core_infinite_delta_inside_a_replay_window(disc):
     """+Inf in delta a few steps before a segment start, so dv = +Inf lies
-    inside the window the segment replays (its backward walk stops there) and
-    the replay's remaining sum of dv is infinite; every state must still take
-    part in the replay.  This shape is cut into segments of 64 steps of the
-    flattened (column tile, t) space (the library's shortest segment): row
-    1's tiles start segments at every t = 8 (mod 64) for channels 0-63,
-    among them t = 584, and at every t = 44 (mod 64) for channels 64-99,
-    among them t = 620 and 1132.  ZOH:
-    aBar = 0 resets the column there and every output stays finite; EULER:
-    dv B u is infinite, the column is non-finite from there on.  Outputs are
-    compared wherever the oracle is finite."""
+    inside the window the segment replays; aBar = 0 there ends the replay's
+    decay product, and every state must still be rebuilt correctly.  The
+    segment starts of batch row 1's two channel tiles come from the
+    library's own split (mss_time_split).  ZOH: aBar = 0 resets the column
+    there and every output stays finite; EULER: dv B u is infinite, the
+    column is non-finite from there on.  Outputs are compared wherever the
+    oracle is finite."""
     import torch
+    import replay_model as rm
     w = W
     inp = gen.generate(w)
     L = w.seq_len
-    for t, ch in ((612, 70), (1125, 99), (580, 5)):
+    seg = mss.time_split(mss.OP_SELECTIVE_SCAN, batch=w.batch, seq_len=L, d_inner=w.d_inner,
+                         d_state=w.d_state, d_conv=w.d_conv)
+    tiles = (w.d_inner + 63) // 64
+    s_lo = [t for t in rm.segment_starts(1 * tiles + 0, L, seg) if t > 200]
+    s_hi = [t for t in rm.segment_starts(1 * tiles + 1, L, seg) if t > 200]
+    marks = ((s_hi[6] - 4, 70), (s_hi[14] - 7, 99), (s_lo[5] - 4, 5))
+    for t, ch in marks:
         inp["delta"][1 * L + t, ch] = np.inf
     d = {k: dev(v) for k, v in inp.items()}
     B, D, N = w.batch, w.d_inner, w.d_state
