@@ -261,7 +261,9 @@ int mss_selective_scan_backward(const mss_dims* dims, int disc, const float* u,
  *     ends.  A problem whose mss_workspace_bytes(MSS_OP_SELECTIVE_SCAN_BACKWARD)
  *     exceeds it is refused with MSS_ESCRATCH before anything is launched
  *     (B2 L512 D256 needs 3.3 MiB, B4 L2048 D1024 101 MiB, B8 L2048 D1536
- *     294 MiB: refused).
+ *     294 MiB: refused).  With the forward's checkpoints (MSS_FLAG_CKPT8)
+ *     the backward needs no checkpoint workspace: B8 L2048 D1536 then needs
+ *     102 MiB.
  *   - The call allocates nothing: no hipMalloc, no hipFree, no allocating
  *     library routine.  Its first call on a device looks up the array's
  *     device address (hipGetSymbolAddress, with that device current).

@@ -77,6 +77,10 @@ def test_noalloc_backward_refuses_past_the_array():
     need = mss.workspace_bytes(mss.OP_SELECTIVE_SCAN_BACKWARD, batch=w.batch, seq_len=w.seq_len,
                                d_inner=w.d_inner, d_state=w.d_state)
     assert need > mss.NOALLOC_SCRATCH_BYTES
+    # with the forward's checkpoints the same problem fits
+    assert mss.workspace_bytes(mss.OP_SELECTIVE_SCAN_BACKWARD, batch=w.batch, seq_len=w.seq_len,
+                               d_inner=w.d_inner, d_state=w.d_state,
+                               ckpt8=True) < mss.NOALLOC_SCRATCH_BYTES
     M, D, N = w.M, w.d_inner, w.d_state
     z = torch.zeros
     args = (z((M, D), device="cuda"), z((M, D), device="cuda"), z((D, N), device="cuda"),
