@@ -375,9 +375,12 @@ def workloads_oracle(target_s=3.0):
 
 
 def backward_extras(w, d, stream, reps=5, with_oracle=True):
-    """The backward passes on the same workload (ZOH): the scan backward
-    (main kernel + fixed-order reduction kernel) on u = SiLU(conv(x)) with a
-    seeded N(0, 1) output gradient, then the conv1d + SiLU backward."""
+    """The backward passes on the same workload (ZOH), as training runs them:
+    the forward (the scan on u = SiLU(conv(x))) writes its 8-step state
+    checkpoints, the scan backward starts from them (main kernel + fixed-
+    order reduction kernel; seeded N(0, 1) output gradient); then the
+    conv1d + SiLU backward.  The scan backward without checkpoints (it then
+    rebuilds the forward states itself) is timed beside."""
     import torch
     import mamba_selective_scan_causal_amd as mss
     from mamba_selective_scan_causal_amd import inputs as gen
@@ -386,16 +389,35 @@ def backward_extras(w, d, stream, reps=5, with_oracle=True):
                         stream=stream)
     dout = torch.from_numpy(gen.cotangent(w)).cuda()
     kw = dict(batch=w.batch, seq_len=w.seq_len, stream=stream)
+    y = torch.empty((M, D), device="cuda")
+    ck = torch.empty((w.batch, mss.ckpt_steps(w.seq_len), D, N), device="cuda")
+
+    def fwd_ck():
+        mss.selective_scan(u, d["delta"], d["A_log"], d["B"], d["C"], d["D_vec"], d["z"], None,
+                           disc="zoh", out=y, h_cache=ck, ckpt8=True, **kw)
+    t_fwd_ck = _time_ms(fwd_ck, stream, reps)
+    t_core_ck = _time_ms(lambda: mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"],
+                                                 d["A_log"], d["B"], d["C"], d["D_vec"], d["z"],
+                                                 None, disc="zoh", out=y, h_cache=ck,
+                                                 ckpt8=True, **kw), stream, reps)
     nb = mss.workspace_bytes(mss.OP_SELECTIVE_SCAN_BACKWARD, batch=w.batch, seq_len=w.seq_len,
                              d_inner=D, d_state=N)
+    nb_ck = mss.workspace_bytes(mss.OP_SELECTIVE_SCAN_BACKWARD, batch=w.batch,
+                                seq_len=w.seq_len, d_inner=D, d_state=N, ckpt8=True)
     ws = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
     box = {}
 
-    def sb():
+    def sb_ck():
         box["g"] = mss.selective_scan_backward(u, d["delta"], d["A_log"], d["B"], d["C"],
                                                d["D_vec"], d["z"], None, dout, disc="zoh",
-                                               workspace=ws, **kw)
-    t_sb = _time_ms(sb, stream, reps)
+                                               workspace=ws, h_ckpt=ck, **kw)
+
+    def sb():
+        mss.selective_scan_backward(u, d["delta"], d["A_log"], d["B"], d["C"], d["D_vec"],
+                                    d["z"], None, dout, disc="zoh", workspace=ws, **kw)
+    fwd_ck()
+    t_sb = _time_ms(sb_ck, stream, reps)
+    t_sb_plain = _time_ms(sb, stream, reps)
     du = box["g"]["du"]
     nc = mss.workspace_bytes(mss.OP_CONV1D_SILU_BACKWARD, batch=w.batch, seq_len=w.seq_len,
                              d_inner=D, d_state=1, d_conv=w.d_conv)
@@ -406,10 +428,17 @@ def backward_extras(w, d, stream, reps=5, with_oracle=True):
     # B, C in and dB, dC out per (m, n); x, du in and dx out for the conv
     sb_bytes = 4 * (7 * M * D + 4 * M * N + 3 * D * N + 2 * D)
     cb_bytes = 4 * (3 * M * D + 2 * D * (w.d_conv + 1))
-    res = {"disc": "zoh", "workspace_bytes": nb,
-           "scan_backward_ms": t_sb, "scan_backward_algorithmic_bytes": sb_bytes,
+    res = {"disc": "zoh",
+           "scan_backward_ms": t_sb,
+           "scan_backward_note": "from the forward's 8-step state checkpoints (MSS_FLAG_CKPT8)",
+           "workspace_bytes": nb_ck,
+           "scan_backward_algorithmic_bytes": sb_bytes,
            "scan_backward_GBps": sb_bytes / t_sb / 1e6,
            "scan_backward_elements_per_s": M * D / (t_sb / 1e3),
+           "scan_backward_without_checkpoints_ms": t_sb_plain,
+           "workspace_bytes_without_checkpoints": nb,
+           "forward_scan_with_checkpoints_ms": t_fwd_ck,
+           "fused_core_with_checkpoints_ms": t_core_ck,
            "conv1d_silu_backward_ms": t_cb, "conv1d_silu_backward_GBps": cb_bytes / t_cb / 1e6,
            "total_ms": t_sb + t_cb}
     if with_oracle:

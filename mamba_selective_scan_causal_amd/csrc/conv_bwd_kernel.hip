@@ -28,6 +28,74 @@ __device__ __forceinline__ float silu_grad(float v) {
     return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
 }
 
+// dx and the dw, db sums over the kRun steps of one run.  In the last run of
+// a row (TAIL) the steps past the end take no part: the x repeated there may
+// be non-finite, so they are skipped rather than multiplied by zero.  The
+// guard is uniform across the wave; it is a separate instantiation so that
+// full runs carry no per-step test.
+// x at t0 - (KR - 1) .. t0 + kRun + KR - 2 and dc = du * SiLU'(c) at
+// t0 .. t0 + kRun + KR - 2 for one run.  EDGE: the run touches an end of the
+// row, so indices are clamped into it, x before the start is 0 and dc past
+// the end is 0 (a select, not a product: the x repeated there may be
+// non-finite).
+template <int KR, bool EDGE>
+__device__ __forceinline__ void load_run(const ConvBwdArgs& a, const float (&w)[KR], float bias,
+                                         float (&xv)[kRun + 2 * (KR - 1)],
+                                         float (&dc)[kRun + KR - 1], int64_t base, int64_t t0) {
+    constexpr int NX = kRun + 2 * (KR - 1), NC = kRun + KR - 1;
+    const int64_t L = a.L, D = a.D;
+    float gv[NC];
+    if (EDGE) {
+#pragma unroll
+        for (int i = 0; i < NX; i++) {
+            const int64_t t = t0 - (KR - 1) + i;
+            const int64_t tc = t < 0 ? 0 : (t < L ? t : L - 1);
+            const float v = a.x[base + tc * D];
+            xv[i] = t >= 0 ? v : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+            const int64_t t = t0 + i;
+            const float v = a.du[base + (t < L ? t : L - 1) * D];
+            gv[i] = t < L ? v : 0.0f;
+        }
+    } else {
+        const float* xp = a.x + base + (t0 - (KR - 1)) * D;
+        const float* gp = a.du + base + t0 * D;
+#pragma unroll
+        for (int i = 0; i < NX; i++) xv[i] = xp[i * D];
+#pragma unroll
+        for (int i = 0; i < NC; i++) gv[i] = gp[i * D];
+    }
+#pragma unroll
+    for (int i = 0; i < NC; i++) {
+        float c = bias;
+#pragma unroll
+        for (int k = 0; k < KR; k++) c = __builtin_fmaf(w[k], xv[i + KR - 1 - k], c);
+        const float v = gv[i] * silu_grad(c);
+        dc[i] = EDGE && t0 + i >= L ? 0.0f : v;
+    }
+}
+
+template <int KR, bool TAIL>
+__device__ __forceinline__ void run_steps(const ConvBwdArgs& a, const float (&w)[KR],
+                                          const float (&xv)[kRun + 2 * (KR - 1)],
+                                          const float (&dc)[kRun + KR - 1], float (&sw)[KR],
+                                          float& sb, int64_t base, int64_t t0, bool live) {
+#pragma unroll
+    for (int i = 0; i < kRun; i++) {
+        const int64_t t = t0 + i;
+        if (TAIL && t >= a.L) continue;
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], dc[i + k], acc);
+        if (live) a.dx[base + t * a.D] = acc;
+        sb += dc[i];
+#pragma unroll
+        for (int k = 0; k < KR; k++) sw[k] = __builtin_fmaf(dc[i], xv[i + KR - 1 - k], sw[k]);
+    }
+}
+
 template <int K>
 __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
     constexpr int KR = K;
@@ -53,42 +121,16 @@ __global__ __launch_bounds__(kWave) void conv_bwd_kernel(ConvBwdArgs a) {
         const int64_t b = job / runs;
         const int64_t t0 = (job - b * runs) * kRun;
         const int64_t base = b * L * D + d;
-        float xv[NX], gv[NC];
-#pragma unroll
-        for (int i = 0; i < NX; i++) {
-            const int64_t t = t0 - (KR - 1) + i;
-            const int64_t tc = t < 0 ? 0 : (t < L ? t : L - 1);
-            const float v = a.x[base + tc * D];
-            xv[i] = t >= 0 ? v : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < NC; i++) {
-            const int64_t t = t0 + i;
-            const float v = a.du[base + (t < L ? t : L - 1) * D];
-            gv[i] = t < L ? v : 0.0f;
-        }
-        float dc[NC];
-#pragma unroll
-        for (int i = 0; i < NC; i++) {
-            float c = bias;
-#pragma unroll
-            for (int k = 0; k < KR; k++) c = __builtin_fmaf(w[k], xv[i + KR - 1 - k], c);
-            // 0 past the sequence end (a select, not a product: the x
-            // repeated there may be non-finite)
-            dc[i] = t0 + i < L ? gv[i] * silu_grad(c) : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < kRun; i++) {
-            const int64_t t = t0 + i;
-            float acc = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], dc[i + k], acc);
-            if (t >= L) break;   // wave-uniform: only the last run of a row is short
-            if (live) a.dx[base + t * D] = acc;
-            sb += dc[i];
-#pragma unroll
-            for (int k = 0; k < KR; k++) sw[k] = __builtin_fmaf(dc[i], xv[i + KR - 1 - k], sw[k]);
-        }
+        float xv[NX], dc[NC];
+        // runs that touch neither end of the row load without clamps
+        if (t0 >= KR - 1 && t0 + NC <= L)
+            load_run<KR, false>(a, w, bias, xv, dc, base, t0);
+        else
+            load_run<KR, true>(a, w, bias, xv, dc, base, t0);
+        if (t0 + kRun <= L)
+            run_steps<KR, false>(a, w, xv, dc, sw, sb, base, t0, live);
+        else
+            run_steps<KR, true>(a, w, xv, dc, sw, sb, base, t0, live);
     }
     float* p = a.part + blockIdx.x * static_cast<int64_t>(kPartRows * kWave) + threadIdx.x;
 #pragma unroll
