@@ -140,7 +140,7 @@ int check_dims(const mss_dims* dims, bool need_l, bool need_k) {
 #define MSS_BWD_MIN_SEG 64
 #endif
 #ifndef MSS_SSD_TARGET_WG
-#define MSS_SSD_TARGET_WG 1280       // about five 4-wave workgroups per CU
+#define MSS_SSD_TARGET_WG 1280       // five 4-wave workgroups per CU of 256
 #endif
 #ifndef MSS_SSD_MIN_SEG
 #define MSS_SSD_MIN_SEG 64
@@ -348,7 +348,7 @@ bool ssd_dims_ok(const mss_ssd_dims* dims) {
 }
 
 // SSD segments per (batch row, head): about MSS_SSD_TARGET_WG workgroups in
-// all (two are resident per CU at a time; the surplus evens out the finish),
+// all (three are resident per CU at a time for the common shapes),
 // none shorter than MSS_SSD_MIN_SEG steps (two chunks), so that the replay
 // that rebuilds a segment's initial state does not outweigh its own steps;
 // then rounded so that every segment has the same number of chunks.

@@ -21,12 +21,13 @@
 // S[4 (l/16) + i][l % 16]) exactly the B operand of C S, so the state never
 // leaves the registers between chunks.
 //
-// Mapping.  One workgroup (4 waves) per (batch row, head, time segment).
-// Wave w owns the P columns [16 w c, ...) of S and of y.  Per chunk (its
-// loads issued one chunk ahead into registers): X (transposed), B, B^T
-// weighted by the state weights, C and the decay prefix go to LDS;
-// three waves form the three nonzero 16 x 16 tiles of L o C B^T; each wave
-// then forms its y columns and updates its S columns.  A segment that starts
+// Mapping.  One workgroup (4 waves) per (batch row, head, time segment),
+// three resident per CU for the common shapes (168 registers, under 53 KB of
+// LDS).  Wave w owns the P columns [16 w c, ...) of S and of y.  Per chunk
+// (its loads issued one chunk ahead into registers): X and B transposed, C,
+// the decay prefix and the state weights go to LDS; the four waves share the
+// work of the three nonzero 16 x 16 tiles of L o C B^T; each wave then forms
+// its y columns and updates its S columns.  A segment that starts
 // at t0 > 0 first rebuilds S(t0 - 1) by replaying the state update from the
 // point where every contribution before it has decayed by 2^-c, with
 // c = MSS_REPLAY_DECAY_BITS (for a scalar-decay head the walk is uniform
@@ -48,22 +49,46 @@ __device__ __forceinline__ v4f mfma(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Global-memory pointers: accesses through them are global (not flat)
+// instructions, which do not hold up the waits on LDS reads.
+typedef const __attribute__((address_space(1))) float* gptr;
+typedef const __attribute__((address_space(1))) v4f* gptr4;
+
+// p + off as a scalar base the compiler cannot see through (so it is not
+// split into one induction pointer per access).
+__device__ __forceinline__ gptr gbase(const float* p, int64_t off) {
+    gptr q = (gptr)(p) + off;
+    asm volatile("" : "+s"(q));
+    return q;
+}
+
 template <int P, int N>
 struct Cfg {
     static constexpr int CT = P / 16;                   // column tiles of P
     static constexpr int CTW = CT >= kWaves ? CT / kWaves : 1;   // per wave
     static constexpr int NT = N / 16;
     static constexpr int LDN = N + 4;                   // C, B rows (floats)
-    static constexpr int LDQ = kQ + 4;                  // Bt, Xt, G rows
+    static constexpr int LDQ = kQ + 4;                  // Bt, Xt rows
+    static constexpr int LDG = 16 + 4;                  // rows of a G tile
+    static constexpr int GT = 16 * LDG;                 // one G tile (floats)
+    // The three nonzero 16 x 16 tiles of L o C B^T (rows 0-15 x columns
+    // 0-15, rows 16-31 x columns 0-15, rows 16-31 x columns 16-31) are
+    // spread evenly over the four waves when the k tiles divide (BAL): each
+    // tile is then the sum of two partial tiles, one in GA and one in GB.
+    static constexpr bool BAL = NT % 4 == 0;
+    // Waves per SIMD the registers are budgeted for: three workgroups per
+    // CU (168 registers) where the state and the staged chunk fit in them.
+    static constexpr int kWpe = P == 128 ? (N >= 128 ? 1 : N >= 64 ? 2 : 3) : 3;
     // LDS layout (floats)
     static constexpr int oC = 0;
-    static constexpr int oB = oC + kQ * LDN;
-    static constexpr int oBt = oB + kQ * LDN;
+    static constexpr int oBt = oC + kQ * LDN;
     static constexpr int oXt = oBt + N * LDQ;
-    static constexpr int oG = oXt + P * LDQ;
-    static constexpr int oCum = oG + kQ * LDQ;
+    static constexpr int oGA = oXt + P * LDQ;
+    static constexpr int oGB = oGA + 3 * GT;
+    static constexpr int oCum = oGB + (BAL ? 3 * GT : 0);
     static constexpr int oDv = oCum + kQ;
-    static constexpr int oMisc = oDv + kQ;
+    static constexpr int oW = oDv + kQ;
+    static constexpr int oMisc = oW + kQ;
     static constexpr int total = oMisc + 4;
 };
 
@@ -95,49 +120,50 @@ struct Ssd {
     static constexpr int kXv = (kQ * (P / 4) + kThreads - 1) / kThreads;   // float4 per thread
     static constexpr int kBv = (kQ * (N / 4) + kThreads - 1) / kThreads;
     struct Stage {
-        float4 xv[kXv], bv[kBv], cv[kBv];
+        v4f xv[kXv], bv[kBv], cv[kBv];
         float dt;
     };
 
     // Loads of chunk [t0, t0 + kQ) (zeros past the sequence end, where dv = 0
-    // leaves S unchanged and no output is written).  full: also C.
+    // leaves S unchanged and no output is written).  full: also C.  Each
+    // tensor is read from the chunk's first row (a scalar base, made opaque
+    // so that the compiler keeps one base instead of one pointer per load)
+    // plus this lane's fixed offset; load k sits 32 floats past load k - 1.
     __device__ __forceinline__ void issue(Stage& st, int64_t t0, bool full) const {
         const int tid = threadIdx.x;
         const int64_t HP = a.H * P, GN = a.G * N;
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int j = tid % kQ;
+        const bool in = t0 + j < a.L;
+        gptr xb = gbase(a.x, row(t0) * HP + h * P);
+        gptr bb = gbase(a.Bm, row(t0) * GN + g * N);
+        gptr cb = gbase(a.Cm, row(t0) * GN + g * N);
+        const int64_t ox = j * HP + (tid / kQ) * 4, ob = j * GN + (tid / kQ) * 4;
+        constexpr int kStep = (kThreads / kQ) * 4;
 #pragma unroll
         for (int k = 0; k < kXv; k++) {
-            const int i = tid + k * kThreads;
-            const int j = i % kQ, p4 = (i / kQ) * 4;
-            const int64_t t = t0 + j;
-            float4 v = z4;
-            if (i < kQ * (P / 4) && t < a.L)
-                v = *reinterpret_cast<const float4*>(a.x + row(t) * HP + h * P + p4);
+            v4f v = {0.f, 0.f, 0.f, 0.f};
+            if (tid + k * kThreads < kQ * (P / 4) && in)
+                v = *reinterpret_cast<gptr4>(xb + ox + k * kStep);
             st.xv[k] = v;
         }
 #pragma unroll
         for (int k = 0; k < kBv; k++) {
-            const int i = tid + k * kThreads;
-            const int j = i % kQ, n4 = (i / kQ) * 4;
-            const int64_t t = t0 + j;
-            const bool ok = i < kQ * (N / 4) && t < a.L;
-            const int64_t o = row(ok ? t : 0) * GN + g * N + n4;
-            float4 vb = z4, vc = z4;
-            if (ok) {
-                vb = *reinterpret_cast<const float4*>(a.Bm + o);
-                if (full) vc = *reinterpret_cast<const float4*>(a.Cm + o);
+            v4f vb = {0.f, 0.f, 0.f, 0.f}, vc = vb;
+            if (tid + k * kThreads < kQ * (N / 4) && in) {
+                vb = *reinterpret_cast<gptr4>(bb + ob + k * kStep);
+                if (full)
+                    vc = *reinterpret_cast<gptr4>(cb + ob + k * kStep);
             }
             st.bv[k] = vb;
             st.cv[k] = vc;
         }
         // every thread loads dt of its step (tid % kQ)
-        const int64_t t = t0 + (tid % kQ);
         float dtv = 0.0f;
-        if (t < a.L) dtv = a.dt[row(t) * a.H + h];
+        if (in) dtv = a.dt[row(t0 + j) * a.H + h];
         st.dt = dtv;
     }
 
-    // Staged chunk into LDS: Xt (transposed), B, Bt, C, and dv, the decay
+    // Staged chunk into LDS: Xt and Bt (transposed), C, and f, the decay
     // prefix c (log2 units) and the state weights.  Ends with a barrier.
     __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
         const int tid = threadIdx.x;
@@ -165,6 +191,7 @@ struct Ssd {
         if (tid < kQ) {
             lds[C_::oCum + tid] = cj;
             lds[C_::oDv + tid] = fj;
+            lds[C_::oW + tid] = wj;
         }
         float* xt = lds + C_::oXt;
 #pragma unroll
@@ -183,50 +210,71 @@ struct Ssd {
             const int i = tid + k * kThreads;
             if (i >= kQ * (N / 4)) break;
             const int j = i % kQ, n4 = (i / kQ) * 4;
-            *reinterpret_cast<float4*>(lds + C_::oB + j * C_::LDN + n4) = st.bv[k];
-            *reinterpret_cast<float4*>(lds + C_::oC + j * C_::LDN + n4) = st.cv[k];
-            // Bt holds B^T already weighted by w_j (its only use)
-            bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x * wj;
-            bt[(n4 + 1) * C_::LDQ + j] = st.bv[k].y * wj;
-            bt[(n4 + 2) * C_::LDQ + j] = st.bv[k].z * wj;
-            bt[(n4 + 3) * C_::LDQ + j] = st.bv[k].w * wj;
+            *reinterpret_cast<v4f*>(lds + C_::oC + j * C_::LDN + n4) = st.cv[k];
+            bt[(n4 + 0) * C_::LDQ + j] = st.bv[k].x;
+            bt[(n4 + 1) * C_::LDQ + j] = st.bv[k].y;
+            bt[(n4 + 2) * C_::LDQ + j] = st.bv[k].z;
+            bt[(n4 + 3) * C_::LDQ + j] = st.bv[k].w;
         }
         __syncthreads();
     }
 
-    // L o C B^T: the three nonzero 16 x 16 tiles (waves 0-2); wave 3 writes
-    // the zero tile above the diagonal.
-    __device__ __forceinline__ void form_g() const {
-        const float* cum = lds + C_::oCum;
-        const float* dvs = lds + C_::oDv;
-        float* G = lds + C_::oG;
-        if (wave == 3) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) G[(4 * g4 + i) * C_::LDQ + 16 + q16] = 0.0f;
-            return;
-        }
-        const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+    // Partial G tile T (0: rows 0-15 x columns 0-15, 1: rows 16-31 x
+    // columns 0-15, 2: rows 16-31 x columns 16-31) over the k tiles
+    // [K0, K1) of N, scaled by 2^{c_i - c_j} f_j and masked to i >= j, into
+    // tile T of dst.
+    template <int T, int K0, int K1>
+    __device__ __forceinline__ void g_part(float* dst) const {
+        constexpr int ti = T == 0 ? 0 : 1, tj = T == 2 ? 1 : 0;
         // two accumulators over alternating halves of each k tile, added at
         // the end (independent chains for the matrix pipe)
         v4f acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
         const float* Cr = lds + C_::oC + (16 * ti + q16) * C_::LDN + 4 * g4;
-        const float* Br = lds + C_::oB + (16 * tj + q16) * C_::LDN + 4 * g4;
+        const float* Bc = lds + C_::oBt + 4 * g4 * C_::LDQ + 16 * tj + q16;
 #pragma unroll
-        for (int kt = 0; kt < C_::NT; kt++) {
+        for (int kt = K0; kt < K1; kt++) {
             const float4 ca = *reinterpret_cast<const float4*>(Cr + 16 * kt);
-            const float4 bb = *reinterpret_cast<const float4*>(Br + 16 * kt);
-            acc = mfma(ca.x, bb.x, acc);
-            acc2 = mfma(ca.y, bb.y, acc2);
-            acc = mfma(ca.z, bb.z, acc);
-            acc2 = mfma(ca.w, bb.w, acc2);
+            const float* B0 = Bc + 16 * kt * C_::LDQ;
+            acc = mfma(ca.x, B0[0], acc);
+            acc2 = mfma(ca.y, B0[C_::LDQ], acc2);
+            acc = mfma(ca.z, B0[2 * C_::LDQ], acc);
+            acc2 = mfma(ca.w, B0[3 * C_::LDQ], acc2);
         }
         acc += acc2;
+        const float* cum = lds + C_::oCum;
         const int j = 16 * tj + q16;
-        const float cj = cum[j], dj = dvs[j];
+        const float cj = cum[j], dj = lds[C_::oDv + j];
+        float* G = dst + T * C_::GT + q16;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int i = 16 * ti + 4 * g4 + r;
-            G[i * C_::LDQ + j] = i >= j ? acc[r] * ex2(cum[i] - cj) * dj : 0.0f;
+            G[(4 * g4 + r) * C_::LDG] = i >= j ? acc[r] * ex2(cum[i] - cj) * dj : 0.0f;
+        }
+    }
+
+    // L o C B^T.  BAL: the 3 NT (tile, k tile) products in that order are
+    // cut into four equal runs, one per wave; wave w's part of tile T goes
+    // to GA when T = w, else to GB.  Otherwise waves 0-2 form one whole
+    // tile each, into GA.
+    __device__ __forceinline__ void form_g() const {
+        constexpr int NT = C_::NT;
+        float* GA = lds + C_::oGA;
+        float* GB = lds + C_::oGB;
+        if constexpr (C_::BAL) {
+            constexpr int R = 3 * NT / 4;
+            switch (wave) {
+                case 0: g_part<0, 0, R>(GA); break;
+                case 1: g_part<0, R, NT>(GB); g_part<1, 0, 2 * R - NT>(GA); break;
+                case 2: g_part<1, 2 * R - NT, NT>(GB); g_part<2, 0, 3 * R - 2 * NT>(GA); break;
+                default: g_part<2, 3 * R - 2 * NT, NT>(GB); break;
+            }
+        } else {
+            switch (wave) {
+                case 0: g_part<0, 0, NT>(GA); break;
+                case 1: g_part<1, 0, NT>(GA); break;
+                case 2: g_part<2, 0, NT>(GA); break;
+                default: break;
+            }
         }
     }
 
@@ -236,7 +284,6 @@ struct Ssd {
     // once to the finished tile instead of to every operand.
     __device__ __forceinline__ void output(const v4f (&S)[C_::CTW][C_::NT], int64_t t0,
                                            int nout) const {
-        const float* G = lds + C_::oG;
         const float* Xt = lds + C_::oXt;
         const float* Cc = lds + C_::oC;
         const float* cum = lds + C_::oCum;
@@ -247,28 +294,46 @@ struct Ssd {
             f0[r] = ex2(cum[4 * g4 + r]);
             f1[r] = ex2(cum[16 + 4 * g4 + r]);
         }
+        // this lane's A operands of the three G tiles (the same for every
+        // column tile), partial tiles added
+        float4 g00, g10, g11;
+        {
+            const float* ga = lds + C_::oGA + q16 * C_::LDG + 4 * g4;
+            g00 = *reinterpret_cast<const float4*>(ga);
+            g10 = *reinterpret_cast<const float4*>(ga + C_::GT);
+            g11 = *reinterpret_cast<const float4*>(ga + 2 * C_::GT);
+            if constexpr (C_::BAL) {
+                const float* gb = ga + (C_::oGB - C_::oGA);
+                const float4 b00 = *reinterpret_cast<const float4*>(gb);
+                const float4 b10 = *reinterpret_cast<const float4*>(gb + C_::GT);
+                const float4 b11 = *reinterpret_cast<const float4*>(gb + 2 * C_::GT);
+                g00 = make_float4(g00.x + b00.x, g00.y + b00.y, g00.z + b00.z, g00.w + b00.w);
+                g10 = make_float4(g10.x + b10.x, g10.y + b10.y, g10.z + b10.z, g10.w + b10.w);
+                g11 = make_float4(g11.x + b11.x, g11.y + b11.y, g11.z + b11.z, g11.w + b11.w);
+            }
+        }
 #pragma unroll
         for (int c = 0; c < C_::CTW; c++) {
             const int ct = wave * C_::CTW + c;
             if (ct >= C_::CT) break;
             v4f y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, o0 = y0, o1 = y0;
-            const float* G0 = G + q16 * C_::LDQ + 4 * g4;
-            const float* G1 = G0 + 16 * C_::LDQ;
             const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
-#pragma unroll
-            for (int kt = 0; kt < kQ / 16; kt++) {
-                const float4 xb = *reinterpret_cast<const float4*>(Xr + 16 * kt);
-                const float4 g0 = *reinterpret_cast<const float4*>(G0 + 16 * kt);
-                const float4 g1 = *reinterpret_cast<const float4*>(G1 + 16 * kt);
-                y0 = mfma(g0.x, xb.x, y0);
-                y1 = mfma(g1.x, xb.x, y1);
-                y0 = mfma(g0.y, xb.y, y0);
-                y1 = mfma(g1.y, xb.y, y1);
-                y0 = mfma(g0.z, xb.z, y0);
-                y1 = mfma(g1.z, xb.z, y1);
-                y0 = mfma(g0.w, xb.w, y0);
-                y1 = mfma(g1.w, xb.w, y1);
-            }
+            // rows 0-15 see only the first 16 steps (the tile right of the
+            // diagonal is zero and skipped)
+            const float4 xb0 = *reinterpret_cast<const float4*>(Xr);
+            const float4 xb1 = *reinterpret_cast<const float4*>(Xr + 16);
+            y0 = mfma(g00.x, xb0.x, y0);
+            y1 = mfma(g10.x, xb0.x, y1);
+            y0 = mfma(g00.y, xb0.y, y0);
+            y1 = mfma(g10.y, xb0.y, y1);
+            y0 = mfma(g00.z, xb0.z, y0);
+            y1 = mfma(g10.z, xb0.z, y1);
+            y0 = mfma(g00.w, xb0.w, y0);
+            y1 = mfma(g10.w, xb0.w, y1);
+            y1 = mfma(g11.x, xb1.x, y1);
+            y1 = mfma(g11.y, xb1.y, y1);
+            y1 = mfma(g11.z, xb1.z, y1);
+            y1 = mfma(g11.w, xb1.w, y1);
             const float* C0 = Cc + q16 * C_::LDN + 4 * g4;
             const float* C1 = C0 + 16 * C_::LDN;
 #pragma unroll
@@ -290,20 +355,34 @@ struct Ssd {
             const float4 x0 = *reinterpret_cast<const float4*>(Xt + p * C_::LDQ + 4 * g4);
             const float4 x1 = *reinterpret_cast<const float4*>(Xt + p * C_::LDQ + 16 + 4 * g4);
             const float xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+            gptr yb = gbase(a.y, row(t0) * HP + h * P);
+            auto* yr = const_cast<__attribute__((address_space(1))) float*>(yb) +
+                       (static_cast<int64_t>(4 * g4) * HP + p);
+            float v0[4], v1[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int i0 = 4 * g4 + r, i1 = 16 + 4 * g4 + r;
-                if (i0 < nout)
-                    a.y[row(t0 + i0) * HP + h * P + p] =
-                        __builtin_fmaf(dskip, xs0[r], __builtin_fmaf(f0[r], o0[r], y0[r]));
-                if (i1 < nout)
-                    a.y[row(t0 + i1) * HP + h * P + p] =
-                        __builtin_fmaf(dskip, xs1[r], __builtin_fmaf(f1[r], o1[r], y1[r]));
+                v0[r] = __builtin_fmaf(dskip, xs0[r], __builtin_fmaf(f0[r], o0[r], y0[r]));
+                v1[r] = __builtin_fmaf(dskip, xs1[r], __builtin_fmaf(f1[r], o1[r], y1[r]));
+            }
+            if (nout == kQ) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    yr[r * HP] = v0[r];
+                    yr[(16 + r) * HP] = v1[r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    if (4 * g4 + r < nout) yr[r * HP] = v0[r];
+                    if (16 + 4 * g4 + r < nout) yr[(16 + r) * HP] = v1[r];
+                }
             }
         }
     }
 
-    // S <- e^{c_{Q-1}} S + sum_j w_j B_j^T x_j (this wave's columns).
+    // S <- e^{c_{Q-1}} S + sum_j B_j^T (w_j x_j) (this wave's columns; the
+    // weights go on the x operand in registers, so Bt stays unweighted for
+    // the C B^T tiles).
     __device__ __forceinline__ void update(v4f (&S)[C_::CTW][C_::NT]) const {
         const float decay = ex2(lds[C_::oCum + kQ - 1]);
         const float* Bt = lds + C_::oBt;
@@ -315,8 +394,11 @@ struct Ssd {
             const float* Xr = Xt + (16 * ct + q16) * C_::LDQ + 4 * g4;
             float4 xb[kQ / 16];
 #pragma unroll
-            for (int kt = 0; kt < kQ / 16; kt++)
-                xb[kt] = *reinterpret_cast<const float4*>(Xr + 16 * kt);
+            for (int kt = 0; kt < kQ / 16; kt++) {
+                const float4 wv = *reinterpret_cast<const float4*>(lds + C_::oW + 16 * kt + 4 * g4);
+                const float4 xv = *reinterpret_cast<const float4*>(Xr + 16 * kt);
+                xb[kt] = make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+            }
 #pragma unroll
             for (int tn = 0; tn < C_::NT; tn++) {
                 v4f s = S[c][tn] * decay;
@@ -371,7 +453,8 @@ struct Ssd {
 };
 
 template <int P, int N>
-__global__ __launch_bounds__(kThreads) void ssd_kernel(SsdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<P, N>::kWpe)))
+void ssd_kernel(SsdArgs a) {
     using C_ = Cfg<P, N>;
     __shared__ __align__(16) float lds[C_::total];
     const int64_t wg = blockIdx.x;

@@ -137,3 +137,33 @@ def test_ssd_full_size_sampled_heads():
     assert_close(hl2[:, heads], ohl2, "h_last (zoh)")
     assert_close(y[:, cols], oy, "y")
     assert_close(hl[:, heads], ohl, "h_last")
+
+
+GUARD_CASES = [
+    ("l100_p16_n32_g2", dict(batch=1, seq_len=100, n_heads=4, head_dim=16, d_state=32, n_groups=2)),
+    ("l77_p64_n128", dict(batch=2, seq_len=77, n_heads=4, head_dim=64, d_state=128)),
+    ("l33_p128_n64", dict(batch=1, seq_len=33, n_heads=2, head_dim=128, d_state=64)),
+    ("l1_p32_n16", dict(batch=3, seq_len=1, n_heads=2, head_dim=32, d_state=16)),
+]
+
+
+@pytest.mark.parametrize("name,over", GUARD_CASES, ids=[c[0] for c in GUARD_CASES])
+def test_ssd_writes_nothing_past_its_output(name, over):
+    """y is the first M rows of a NaN-filled buffer 64 rows longer: the
+    rows past the last chunk's end (a partial chunk here) are never written,
+    and y itself matches the oracle."""
+    import torch
+    w = gen.SSD_SMALL.with_(**over)
+    inp = gen.generate_ssd(w)
+    d = {k: dev(v) for k, v in inp.items()}
+    HP = w.n_heads * w.head_dim
+    buf = nan_like((w.M + 64, HP))
+    y = buf[:w.M]
+    mss.ssd_scan(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D_vec"], d["dt_bias"],
+                 d.get("h0"), batch=w.batch, seq_len=w.seq_len, head_dim=w.head_dim,
+                 d_state=w.d_state, n_groups=w.n_groups, disc="euler", out=y)
+    torch.cuda.synchronize()
+    tail = host(buf[w.M:])
+    assert np.isnan(tail).all(), f"{int((~np.isnan(tail)).sum())} guard values written"
+    oy, _ = oracle_ssd(inp, w)
+    assert_close(host(y), oy, "y")
