@@ -157,19 +157,18 @@ struct Ssd {
             st.bv[k] = vb;
             st.cv[k] = vc;
         }
-        // every thread loads dt of its step (tid % kQ)
+        // wave 0 loads dt of its step (tid % kQ)
         float dtv = 0.0f;
-        if (in) dtv = a.dt[row(t0 + j) * a.H + h];
+        if (wave == 0 && in) dtv = a.dt[row(t0 + j) * a.H + h];
         st.dt = dtv;
     }
 
-    // Staged chunk into LDS: Xt and Bt (transposed), C, and f, the decay
-    // prefix c (log2 units) and the state weights.  Ends with a barrier.
-    __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
+    // dv, the input factor f, the decay prefix c (log2 units) and the state
+    // weight w_j = 2^{c_{Q-1} - c_j} f_j of step j = tid % kQ into LDS.  Run
+    // by wave 0 alone (each 32-lane half; shuffles of width kQ): the other
+    // waves go straight to the staging stores.
+    __device__ __forceinline__ void decay_terms(const Stage& st, int64_t t0) const {
         const int tid = threadIdx.x;
-        // dv, the input factor f, the decay prefix c (log2 units) and the
-        // state weight w_j = 2^{c_{Q-1} - c_j} f_j of this thread's step
-        // j = tid % kQ, computed by every 32-lane half (shuffles of width kQ).
         const int jj = tid % kQ;
         const float dv = t0 + jj < a.L ? softplus(st.dt + bias) : 0.0f;
         float cj = dv * A2;
@@ -193,6 +192,13 @@ struct Ssd {
             lds[C_::oDv + tid] = fj;
             lds[C_::oW + tid] = wj;
         }
+    }
+
+    // Staged chunk into LDS: Xt and Bt (transposed), C, and f, the decay
+    // prefix c (log2 units) and the state weights.  Ends with a barrier.
+    __device__ __forceinline__ void commit(const Stage& st, int64_t t0) const {
+        const int tid = threadIdx.x;
+        if (wave == 0) decay_terms(st, t0);
         float* xt = lds + C_::oXt;
 #pragma unroll
         for (int k = 0; k < kXv; k++) {
@@ -490,6 +496,9 @@ void ssd_kernel(SsdArgs a) {
         const int64_t t0 = c * kQ;
         sd.commit(st, t0);
         if (c + 1 < c1) sd.issue(st, t0 + kQ, c + 1 >= c0);
+        // The matrix-core phases run at raised wave priority, so that a
+        // SIMD issues them ahead of another workgroup's staging work.
+        __builtin_amdgcn_s_setprio(1);
         if (c >= c0) {
             sd.form_g();
             __syncthreads();
@@ -497,6 +506,7 @@ void ssd_kernel(SsdArgs a) {
             sd.output(S, t0, nout);
         }
         sd.update(S);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
     if (c1 == nchunks && a.h_last) {
