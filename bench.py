@@ -9,11 +9,12 @@ block, inputs resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--disc zoh|euler] [--no-cpu-baseline]
 
 Order of work: the side measurements on the GPU (the other workloads, the
-other discretisation, backward, SSD, decode) run first, then W warm-up steps
-and the K timed steps, then everything that times the CPU oracle.  Under
-this VALU-heavy load the clock settles over the first ~20 calls of a cold
-GPU; running the side measurements first lets the timed steps see the clock
-a continuously loaded GPU runs at.
+other discretisation, backward, SSD, decode) run first, then about 100 ms of
+the step, W warm-up steps and the K timed steps, then everything that times
+the CPU oracle.  The part's clock ramps up over the first ~20 ms of sustained
+load (a cold SSD call measures 1.3-1.4 ms, the twentieth 1.07 ms), so every
+timing here, side measurements included, follows about 100 ms of the same
+work: the figures are those of a continuously loaded GPU.
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, AMD published
 METRIC = "selective-scan M·D elements/s and achieved HBM GB/s (% of peak), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mamba1_core_b4_l8192_d5120.txt")
 COPY_BYTES = 1 << 30                      # calibration copy: 1 GiB read + 1 GiB written
+WARM_MS = 100.0                           # sustained load before each side timing (see _settle)
 KERNEL_SOURCES = ("scan_kernel.hip", "device_math.h", "launch.h")
 
 
@@ -137,12 +139,28 @@ def copy_calibration(reps: int):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
-def _time_ms(fn, stream, reps, warm=2):
-    """Mean hipEvent time of fn() on `stream`, in ms."""
+def _settle(fn, stream, warm, warm_ms):
+    """fn() `warm` times, then again for about `warm_ms` of GPU time: the
+    part's clock ramps up over the first ~20 ms of sustained load (an SSD
+    call measures 1.3-1.4 ms at first, 1.07 ms from about the twentieth), so
+    a timing taken right after host-side work would measure the ramp."""
     import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
     for _ in range(warm):
         fn()
+    b.record(stream)
     torch.cuda.synchronize()
+    per = a.elapsed_time(b) / max(warm, 1)
+    for _ in range(min(2000, int(warm_ms / max(per, 1e-3)) + 1)):
+        fn()
+    torch.cuda.synchronize()
+
+
+def _time_ms(fn, stream, reps, warm=2, warm_ms=WARM_MS):
+    """Mean hipEvent time of fn() on `stream`, in ms, after _settle."""
+    import torch
+    _settle(fn, stream, warm, warm_ms)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):
@@ -236,6 +254,7 @@ def extras(w, inp, d, y, disc, stream):
                                        d["B"], d["C"], d["D_vec"], d["z"], None, disc=m, **kw)
     # alternating rounds, so that both layouts see the same clock
     ts = {k: [] for k in ("s", "d")}
+    _settle(dense(disc), stream, 2, WARM_MS)
     for _ in range(4):
         ts["s"] += _event_times(strided(disc), stream, 5)
         ts["d"] += _event_times(dense(disc), stream, 5)
@@ -349,7 +368,7 @@ def workloads_extras(stream, reps=50):
                 mss.mamba1_core(d["x"], d["w_conv"], d["b_conv"], d["delta"], d["A_log"],
                                 d["B"], d["C"], d["D_vec"], d["z"], None, batch=w.batch,
                                 seq_len=w.seq_len, disc=disc, out=y, h_cache=hc, stream=stream)
-            _event_times(f, stream, 20)
+            _settle(f, stream, 2, WARM_MS)
             ts = _event_times(f, stream, reps)
             ms = float(np.median(ts))
             nb = workload_bytes(w, w.hcache)
@@ -615,6 +634,9 @@ def main():
     extra = None
     if not args.no_extras:
         extra = extras(w, inp, d, y, args.disc, stream)
+    # the clock settles on this kernel (about 100 ms of it) before the W
+    # warm-up steps; the timed region is exactly K steps
+    _settle(step, stream, 1, WARM_MS)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
