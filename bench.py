@@ -140,21 +140,26 @@ def copy_calibration(reps: int):
 
 
 def _settle(fn, stream, warm, warm_ms):
-    """fn() `warm` times, then again for about `warm_ms` of GPU time: the
-    part's clock ramps up over the first ~20 ms of sustained load (an SSD
-    call measures 1.3-1.4 ms at first, 1.07 ms from about the twentieth), so
-    a timing taken right after host-side work would measure the ramp."""
+    """fn() at least `warm` times and until about `warm_ms` of GPU time has
+    passed: the part's clock ramps up over the first ~20 ms of sustained
+    load (an SSD call measures 1.3-1.4 ms at first, 1.07 ms from about the
+    twentieth), so a timing taken right after host-side work would measure
+    the ramp."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(warm):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    per = a.elapsed_time(b) / max(warm, 1)
-    for _ in range(min(2000, int(warm_ms / max(per, 1e-3)) + 1)):
-        fn()
-    torch.cuda.synchronize()
+    n, spent = max(warm, 1), 0.0
+    while True:
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        el = a.elapsed_time(b)
+        spent += el
+        if spent >= warm_ms:
+            return
+        per = max(el / n, 1e-3)
+        n = min(2000, int((warm_ms - spent) / per) + 1)
 
 
 def _time_ms(fn, stream, reps, warm=2, warm_ms=WARM_MS):
@@ -275,58 +280,11 @@ def extras(w, inp, d, y, disc, stream):
                       "scan_on_u_ms": ts[disc], f"scan_on_u_{other}_ms": ts[other],
                       "total_ms": tc + ts[disc]}
     del u
-    dw = gen.DECODE
-    dinp = gen.generate(dw)
-    dd = {k: torch.from_numpy(v).cuda() for k, v in dinp.items()}
-    yd = torch.empty((dw.batch, dw.d_inner), device="cuda")
-
-    def decode64():
-        for s_ in range(dw.seq_len):
-            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
-                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
-                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd,
-                               stream=stream)
-
-    t64 = _time_ms(decode64, stream, 3, warm=1)
-
-    # the same 64 steps captured once as a HIP graph and replayed
-    def decode64_current():
-        for s_ in range(dw.seq_len):
-            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
-                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
-                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        decode64_current()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        decode64_current()
-    t64g = _time_ms(graph.replay, torch.cuda.current_stream(), 3, warm=1)
-    del graph
-
-    def one_step():
-        mss.selective_step(dd["x"][0], dd["z"][0], dd["delta"][0], dd["A_log"], dd["B"][0],
-                           dd["C"][0], dd["D_vec"], dd["w_conv"], dd["b_conv"],
-                           dd["conv_state"], dd["h"], disc=disc, out=yd, stream=stream)
-
-    step_cold = _event_times(one_step, stream, 16, before=lambda: flush.fill_(1.0))
     del flush
+    res["decode"] = decode_extras(disc, stream)
     res["backward"] = backward_extras(w, d, stream, with_oracle=False)
     res["ssd"] = ssd_extras(stream, reps=10, with_oracle=False)
     res["workloads"] = workloads_extras(stream)
-    BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
-    step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
-    res["decode"] = {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
-                     "algorithmic_bytes_per_step": step_bytes,
-                     "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
-                     "note": "h + conv window (~100 MB) fit the 256 MB last-level cache",
-                     "graph_us_per_step": t64g * 1e3 / dw.seq_len,
-                     "cold_us_per_step": _stats([t * 1e3 for t in step_cold]),
-                     "cold_GBps": step_bytes / float(np.median(step_cold)) / 1e6}
     return res
 
 
@@ -391,6 +349,65 @@ def workloads_oracle(target_s=3.0):
         inp = gen.generate(w)
         out[w.name] = cpu_baseline(w, inp, "zoh", target_s=target_s, threads=1)
     return out
+
+
+def decode_extras(disc, stream):
+    """The decode workload (256 sequences x 5120 channels, d_state 16): 64
+    consecutive single-token steps with the state carried in place, the
+    same 64 steps replayed from a captured HIP graph, and 16 single steps
+    each after a 512 MB write (cold last-level cache)."""
+    import torch
+    import mamba_selective_scan_causal_amd as mss
+    from mamba_selective_scan_causal_amd import inputs as gen
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    dw = gen.DECODE
+    dinp = gen.generate(dw)
+    dd = {k: torch.from_numpy(v).cuda() for k, v in dinp.items()}
+    yd = torch.empty((dw.batch, dw.d_inner), device="cuda")
+
+    def decode64():
+        for s_ in range(dw.seq_len):
+            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
+                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
+                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd,
+                               stream=stream)
+
+    t64 = _time_ms(decode64, stream, 3, warm=1)
+
+    # the same 64 steps captured once as a HIP graph and replayed
+    def decode64_current():
+        for s_ in range(dw.seq_len):
+            mss.selective_step(dd["x"][s_], dd["z"][s_], dd["delta"][s_], dd["A_log"],
+                               dd["B"][s_], dd["C"][s_], dd["D_vec"], dd["w_conv"],
+                               dd["b_conv"], dd["conv_state"], dd["h"], disc=disc, out=yd)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode64_current()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode64_current()
+    t64g = _time_ms(graph.replay, torch.cuda.current_stream(), 3, warm=1)
+    del graph
+
+    def one_step():
+        mss.selective_step(dd["x"][0], dd["z"][0], dd["delta"][0], dd["A_log"], dd["B"][0],
+                           dd["C"][0], dd["D_vec"], dd["w_conv"], dd["b_conv"],
+                           dd["conv_state"], dd["h"], disc=disc, out=yd, stream=stream)
+
+    step_cold = _event_times(one_step, stream, 16, before=lambda: flush.fill_(1.0))
+    BD, N, K = dw.batch * dw.d_inner, dw.d_state, dw.d_conv
+    step_bytes = BD * (16 + 8 * N + 8 * (K - 1)) + dw.batch * N * 8 + dw.d_inner * (N + K + 2) * 4
+    return {"workload": dw.name, "steps": dw.seq_len, "us_per_step": t64 * 1e3 / dw.seq_len,
+            "algorithmic_bytes_per_step": step_bytes,
+            "GBps": step_bytes / (t64 / dw.seq_len) / 1e6,
+            "note": "h + conv window (~100 MB) fit the 256 MB last-level cache",
+            "graph_us_per_step": t64g * 1e3 / dw.seq_len,
+            "cold_us_per_step": _stats([t * 1e3 for t in step_cold]),
+            "cold_GBps": step_bytes / float(np.median(step_cold)) / 1e6}
 
 
 def backward_extras(w, d, stream, reps=5, with_oracle=True):
@@ -585,10 +602,11 @@ def main():
                     help="skip the side measurements (other mode, unfused path, decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--part", default="all", choices=("all", "backward", "ssd", "workloads"),
+    ap.add_argument("--part", default="all", choices=("all", "backward", "ssd", "workloads", "decode"),
                     help="backward: only the backward passes on the same workload; ssd: only "
                          "the Mamba-2 SSD scan; workloads: only the fused core on the three "
-                         "smaller workloads (one JSON line of timings, for profiling)")
+                         "smaller workloads; decode: only the decode steps (one JSON line of "
+                         "timings, for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
@@ -609,6 +627,9 @@ def main():
             for name, o in workloads_oracle().items():
                 r[name]["cpu_oracle_1core"] = o
         print(json.dumps(r))
+        return
+    if args.part == "decode":
+        print(json.dumps(decode_extras(args.disc, torch.cuda.current_stream())))
         return
     w = gen.MAMBA_2P8B
     inp = gen.generate(w)
