@@ -167,3 +167,19 @@ def test_ssd_writes_nothing_past_its_output(name, over):
     assert np.isnan(tail).all(), f"{int((~np.isnan(tail)).sum())} guard values written"
     oy, _ = oracle_ssd(inp, w)
     assert_close(host(y), oy, "y")
+
+
+PN = [(p, n) for p in (16, 32, 64, 128) for n in (16, 32, 64, 128)]
+
+
+@pytest.mark.parametrize("P,N", PN, ids=[f"p{p}_n{n}" for p, n in PN])
+def test_ssd_every_head_dim_and_state_size(P, N):
+    """Every (P, N) instantiation -- each has its own split of the C B^T
+    tiles over the waves and its own register budget -- on 150 steps (time
+    segments with replays, a ragged last chunk), h0 and h_last, both
+    discretisations across the set."""
+    i = PN.index((P, N))
+    G = 2 if i % 3 == 0 else 1
+    w = gen.SSD_SMALL.with_(name=f"pn_{P}_{N}", batch=1 + i % 2, seq_len=150, n_heads=2 * G,
+                            head_dim=P, d_state=N, n_groups=G, h0=True, seed_index=300 + i)
+    check(w, disc="zoh" if i % 2 == 0 else "euler")
