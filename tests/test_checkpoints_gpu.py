@@ -175,3 +175,49 @@ def test_exact_forward_checkpoints_feed_exact_backward(disc):
                                           inp["dout"], batch=w.batch, seq_len=w.seq_len,
                                           disc=disc)
     _check({k: host(v) for k, v in g.items()}, want, "exact")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("entry", ("core", "scan"))
+def test_strided_forward_checkpoints(entry, disc):
+    """The strided entry points with MSS_FLAG_CKPT8: x, z as the halves of an
+    (M, 2D) buffer, B, C as an unaligned column range of an (M, R + 2N) one,
+    delta and y as column slices; the checkpoints match the oracle's state
+    cache, nothing outside y's slice is written, and the backward started
+    from them matches the oracle's gradients."""
+    import torch
+    w = gen.SMALL.with_(name="strided_ck", batch=2, seq_len=1203, d_inner=160, h0=True)
+    inp = _inputs(w)
+    M, D, N, B, L, R = w.M, w.d_inner, w.d_state, w.batch, w.seq_len, 5
+    g = np.random.default_rng(16)
+    junk = lambda c: g.standard_normal((M, c)).astype(np.float32)
+    src = inp["x"] if entry == "core" else inp["u"]
+    XZ = dev(np.concatenate([src, inp["z"]], axis=1))
+    XP = dev(np.concatenate([junk(R), inp["B"], inp["C"]], axis=1))
+    DP = dev(np.concatenate([inp["delta"], junk(3)], axis=1))
+    YB = nan_like((M, D + 7))
+    x, z = XZ[:, :D], XZ[:, D:]
+    Bv, Cv = XP[:, R:R + N], XP[:, R + N:]
+    dl, y = DP[:, :D], YB[:, 3:3 + D]
+    ck = nan_like((B, mss.ckpt_steps(L), D, N))
+    d = {k: dev(inp[k]) for k in ("w_conv", "b_conv", "A_log", "D_vec", "h0")}
+    if entry == "core":
+        mss.mamba1_core(x, d["w_conv"], d["b_conv"], dl, d["A_log"], Bv, Cv, d["D_vec"], z,
+                        d["h0"], batch=B, seq_len=L, disc=disc, h_cache=ck, ckpt8=True, out=y)
+    else:
+        mss.selective_scan(x, dl, d["A_log"], Bv, Cv, d["D_vec"], z, d["h0"], batch=B,
+                           seq_len=L, disc=disc, h_cache=ck, ckpt8=True, out=y)
+    torch.cuda.synchronize()
+    oy, ohc, _ = oracle.selective_scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"],
+                                       inp["D_vec"], inp["z"], inp["h0"], batch=B, seq_len=L,
+                                       disc=disc, h_cache=True)
+    assert_close(host(y), oy, "y")
+    assert_close(host(ck), _oracle_ckpt(ohc, inp["h0"], w), "checkpoints")
+    outside = torch.cat([YB[:, :3], YB[:, 3 + D:]], dim=1)
+    assert torch.isnan(outside).all().item(), "wrote outside the y slice"
+    dd = {k: dev(v) for k, v in inp.items()}
+    got = _bwd(dd, w, disc, ck)
+    want = oracle.selective_scan_backward(inp["u"], inp["delta"], inp["A_log"], inp["B"],
+                                          inp["C"], inp["D_vec"], inp["z"], inp["h0"],
+                                          inp["dout"], batch=B, seq_len=L, disc=disc)
+    _check(got, want, "strided checkpoints")
