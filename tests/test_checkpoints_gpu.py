@@ -71,6 +71,7 @@ CK_CASES = [
     gen.SMALL.with_(name="len9", batch=3, seq_len=9, d_inner=64, h0=True),
     gen.SMALL.with_(name="len1", batch=2, seq_len=1, d_inner=33),
     gen.SMALL.with_(name="n5", batch=2, seq_len=300, d_inner=40, d_state=5, h0=True),
+    gen.SMALL.with_(name="k3", batch=2, seq_len=301, d_inner=96, d_conv=3, h0=True),
     gen.MAMBA_130M,
 ]
 
