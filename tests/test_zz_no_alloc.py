@@ -71,6 +71,24 @@ def test_noalloc_backward_matches_workspace_entry_point(disc):
         assert np.array_equal(host(g_again[k]), host(r_big[k])), k
 
 
+@pytest.mark.parametrize("disc", ("zoh", "euler"))
+def test_noalloc_backward_exact_matches_workspace_entry_point(disc):
+    """MSS_FLAG_EXACT (one segment per channel tile, a workspace laid out for
+    it) on the static array, right after a split call has left its own
+    contents there: bit for bit the workspace entry point's answer."""
+    import torch
+    w = gen.SMALL.with_(name="noalloc_exact", batch=2, seq_len=900, d_inner=100, h0=True,
+                        seed_index=9)
+    c = _case(w)
+    kw = dict(batch=w.batch, seq_len=w.seq_len, disc=disc, need_dh0=True)
+    mss.selective_scan_backward_noalloc(*c, **kw)
+    g = mss.selective_scan_backward_noalloc(*c, exact=True, **kw)
+    r = mss.selective_scan_backward(*c, exact=True, **kw)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        assert np.array_equal(host(g[k]), host(r[k])), k
+
+
 def test_noalloc_backward_refuses_past_the_array():
     import torch
     w = gen.MAMBA_130M
