@@ -97,6 +97,10 @@ struct Scan {
     static constexpr int KR = L_t::KR;
     static constexpr bool kFused = KS >= 0;
     static constexpr bool kStage = NS == 16;   // B/C rows staged through LDS
+    // Alternating register sets for the block inputs where they fit without
+    // spilling: dense rows, no state cache, a fixed conv width (the other
+    // instantiations copy the prefetched set instead).
+    static constexpr bool kPingPong = DN && CM == kCacheNone && KS != 0;
 
     const Cols& c;
     const int64_t L, D;
@@ -374,7 +378,34 @@ struct Scan {
                 if constexpr (kStage) lds[threadIdx.x] = load_bc(t);
                 steps1<OUT, kStage>(ln, t, cnt);
             }
+        } else if constexpr (kPingPong) {
+            // Two register sets take turns: a block runs on one while the
+            // next block's inputs load into the other, with no copies between
+            // blocks.
+            float ax[kT], ad[kT], az[kT], bx[kT], bd[kT], bz[kT];
+            float4 abc = load_bc(tb), bbc;
+            load_block<OUT>(ax, ad, az, tb);
+            int64_t t = tb;
+            while (t + kT <= te) {
+                block<OUT>(ln, t, ax, ad, az, abc, bx, bd, bz, bbc);
+                t += kT;
+                if (t + kT > te) {
+                    if (t < te) {
+                        lds[threadIdx.x] = bbc;
+                        steps1<OUT, true>(ln, t, static_cast<int>(te - t));
+                    }
+                    return;
+                }
+                block<OUT>(ln, t, bx, bd, bz, bbc, ax, ad, az, abc);
+                t += kT;
+            }
+            if (t < te) {
+                lds[threadIdx.x] = abc;
+                steps1<OUT, true>(ln, t, static_cast<int>(te - t));
+            }
         } else {
+            // one register set: the prefetched inputs are copied before the
+            // next block's loads reuse it
             float nx[kT], nd[kT], nz[kT];
             float4 nbc = load_bc(tb);
             load_block<OUT>(nx, nd, nz, tb);
@@ -392,28 +423,56 @@ struct Scan {
                 lds[threadIdx.x] = nbc;
                 load_block<OUT>(nx, nd, nz, t + kT);
                 nbc = load_bc(t + kT);
-                // Fast path when every lane's slowest state decays by at least
-                // exp(-kT 2^-6) over the block: the rounding of aBar (absolute
-                // ~3e-8 next to 1) then compounds over at most ~64 steps of
-                // memory, and a single step with tiny dv A adds one such error.
-                if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {
-                    // (checkpoints fall on block ends -- segments start at
-                    // multiples of 8 -- so the straight-line block has no
-                    // branch in it and the checkpoint follows it)
-                    constexpr int OB = OUT == kOutCK ? kOut : OUT;
-#pragma unroll
-                    for (int i = 0; i < kT; i++) step<OB, false, true>(ln, cx[i], dv[i], cz[i], t + i, i);
-                    if constexpr (OUT == kOutCK)
-                        if (t + kT < L)
-                            store_state(ln, c.h_cache + (b * ((L + 7) >> 3) + ((t + kT) >> 3)) * D * N);
-                } else {
-                    steps1<OUT, true>(ln, t, kT);
-                }
+                run_block<OUT>(ln, t, cx, dv, cz, sdv);
             }
             if (t < te) {
                 lds[threadIdx.x] = nbc;
                 steps1<OUT, true>(ln, t, static_cast<int>(te - t));
             }
+        }
+    }
+
+    // One full block [t, t + kT) on the inputs (xs, ds, zs, bc) loaded for
+    // it, with the next block's loads issued into (nx, nd, nz, nbc).
+    template <int OUT>
+    __device__ __forceinline__ void block(L_t& ln, int64_t t, const float (&xs)[kT],
+                                          const float (&ds)[kT], const float (&zs)[kT],
+                                          const float4& bc, float (&nx)[kT], float (&nd)[kT],
+                                          float (&nz)[kT], float4& nbc) const {
+        float dv[kT];
+        float sdv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kT; i++) {
+            dv[i] = softplus(ds[i]);
+            sdv += dv[i];
+        }
+        lds[threadIdx.x] = bc;
+        load_block<OUT>(nx, nd, nz, t + kT);
+        nbc = load_bc(t + kT);
+        run_block<OUT>(ln, t, xs, dv, zs, sdv);
+    }
+
+    // The steps of a full block once its B/C rows are in LDS: straight-line
+    // on the fast path when every lane's slowest state decays by at least
+    // exp(-kT 2^-6) over the block (the rounding of aBar, absolute ~3e-8
+    // next to 1, then compounds over at most ~64 steps of memory, and a
+    // single step with tiny dv A adds one such error), else step by step.
+    template <int OUT>
+    __device__ __forceinline__ void run_block(L_t& ln, int64_t t, const float (&xs)[kT],
+                                              const float (&dv)[kT], const float (&zs)[kT],
+                                              float sdv) const {
+        if (!wave_any(sdv * ln.min_a2 < kT * kSmallX2)) {
+            // (checkpoints fall on block ends -- segments start at
+            // multiples of 8 -- so the straight-line block has no
+            // branch in it and the checkpoint follows it)
+            constexpr int OB = OUT == kOutCK ? kOut : OUT;
+#pragma unroll
+            for (int i = 0; i < kT; i++) step<OB, false, true>(ln, xs[i], dv[i], zs[i], t + i, i);
+            if constexpr (OUT == kOutCK)
+                if (t + kT < L)
+                    store_state(ln, c.h_cache + (b * ((L + 7) >> 3) + ((t + kT) >> 3)) * D * N);
+        } else {
+            steps1<OUT, true>(ln, t, kT);
         }
     }
 
