@@ -32,6 +32,24 @@ constexpr float kSmallX = 0.015625f;          // same ZOH expm1 switch as the sc
 // arithmetic so that their latencies overlap.
 constexpr int kRows = 2;
 
+// Accesses with the nontemporal (streaming) cache hint.  In step16_kernel,
+// x, z, delta, y and the state h go through these; the conv window does not.
+// Measured on B256 D5120 (64 consecutive steps, in place): 36.9 us per step
+// against 42.7 us with every access cached, 45.8 against 52.9 us from a cold
+// last-level cache; hinting the window as well ran 39.9 us, and h alone or
+// the activations alone gained little.  Results are bit-identical: the hint
+// changes caching only.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float ld_nt(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+    __builtin_nontemporal_store(f4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f4v*>(p));
+}
+
 // The value of lane ^ B (B = 1 or 2) inside its quad (DPP quad_perm).
 template <int B>
 __device__ __forceinline__ float quad_xor(float v) {
@@ -147,9 +165,9 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
 #pragma unroll
         for (int r = 0; r < kRows; r++) {
             const int64_t bd = bs[r] * a.D + d;
-            xv[r] = a.x[bd];
-            dl[r] = a.delta[bd];
-            zv[r] = a.z ? a.z[bd] : 0.0f;
+            xv[r] = ld_nt(a.x + bd);
+            dl[r] = ld_nt(a.delta + bd);
+            zv[r] = a.z ? ld_nt(a.z + bd) : 0.0f;
 #pragma unroll
             for (int k = 1; k < KR; k++)
                 prev[r][k - 1] =
@@ -158,7 +176,7 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (pvalid[i]) t = src[i * kWave + lane];
+                if (pvalid[i]) t = ld_nt(src + i * kWave + lane);
                 h[r][i][0] = t.x; h[r][i][1] = t.y; h[r][i][2] = t.z; h[r][i][3] = t.w;
             }
         }
@@ -205,11 +223,11 @@ __global__ __launch_bounds__(kWave) void step16_kernel(StepArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 if (pvalid[i])
-                    dst[i * kWave + lane] = make_float4(h[r][i][0], h[r][i][1], h[r][i][2],
-                                                        h[r][i][3]);
+                    st_nt(dst + i * kWave + lane,
+                          make_float4(h[r][i][0], h[r][i][1], h[r][i][2], h[r][i][3]));
             if (valid) {
                 const int64_t bd = bs[r] * a.D + d;
-                a.y[bd] = a.z ? yv * silu(zv[r]) : yv;
+                st_nt(a.y + bd, a.z ? yv * silu(zv[r]) : yv);
                 // shifted window: position K-1-k now holds the input k-1 steps back
 #pragma unroll
                 for (int k = 1; k < KR; k++)
