@@ -89,7 +89,11 @@ __device__ __forceinline__ void run_steps(const ConvBwdArgs& a, const float (&w)
         float acc = 0.0f;
 #pragma unroll
         for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], dc[i + k], acc);
-        if (live) a.dx[base + t * a.D] = acc;
+        // dx is written once and not read here again: the nontemporal
+        // (streaming) hint measured 0.491 -> 0.475 ms on B4 L8192 D5120
+        // (the same hint on the x and du loads, which neighbouring runs
+        // re-read, 0.486 ms), bit-identical
+        if (live) __builtin_nontemporal_store(acc, &a.dx[base + t * a.D]);
         sb += dc[i];
 #pragma unroll
         for (int k = 0; k < KR; k++) sw[k] = __builtin_fmaf(dc[i], xv[i + KR - 1 - k], sw[k]);
