@@ -36,9 +36,9 @@ constexpr int kRows = 2;
 // x, z, delta, y and the state h go through these; the conv window does not.
 // Measured on B256 D5120 (64 consecutive steps, in place): 36.9 us per step
 // against 42.7 us with every access cached, 45.8 against 52.9 us from a cold
-// last-level cache; hinting the window as well ran 39.9 us, and h alone or
-// the activations alone gained little.  Results are bit-identical: the hint
-// changes caching only.
+// last-level cache; h alone hinted ran 38.3 us, the activations alone
+// 42.5 us, and everything including the window 39.9 us.  Results are
+// bit-identical: the hint changes caching only.
 typedef float f4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float ld_nt(const float* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float4 ld_nt(const float4* p) {
